@@ -1,0 +1,159 @@
+"""CPU oracle for OSC W4A4 linear layers -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The arithmetic lives in ``osc_oracle.c`` (plain
+C, fp64); this module only marshals numpy arrays through ctypes.  See that
+file's header for the passages of the OSC page each function follows.
+
+All bf16 data is passed as raw bit patterns (``numpy.uint16``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+MXFP4 = 0
+MXFP8 = 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        L.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_value.restype = ctypes.c_double
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_decode.restype = ctypes.c_double
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_e2m1_encode.argtypes = [ctypes.c_double]
+        L.orc_e2m1_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_double]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_scale_exp.argtypes = [ctypes.c_double, i]
+        L.orc_scale_exp.restype = i
+        L.orc_quant_act.argtypes = [P, i, i, i, P, i, P, P, P]
+        L.orc_quant_act.restype = None
+        L.orc_pack_weights.argtypes = [P, i, i, i, P, i, P, P, P]
+        L.orc_pack_weights.restype = None
+        L.orc_gemm.argtypes = [P, P, i, P, P, P, i, P, i, i, i, i, P]
+        L.orc_gemm.restype = None
+        L.orc_build_table.argtypes = [P, i, i, i, ctypes.c_double, ctypes.c_double, P, P, P]
+        L.orc_build_table.restype = i
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------ scalar codecs
+
+def bf16_value(bits: int) -> float:
+    return lib().orc_bf16_value(int(bits))
+
+
+def e2m1_decode(code: int) -> float:
+    return lib().orc_e2m1_decode(int(code))
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(int(code))
+
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().orc_e2m1_encode(float(v)))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().orc_e4m3_encode(float(v)))
+
+
+def scale_exp(amax: float, fmt: int) -> int:
+    return int(lib().orc_scale_exp(float(amax), int(fmt)))
+
+
+# ------------------------------------------------------------ array entry points
+
+def code_bytes_per_row(H: int, fmt: int) -> int:
+    return H // 2 if fmt == MXFP4 else H
+
+
+def quant_act(X: np.ndarray, G: int, L: Optional[np.ndarray], fmt: int = MXFP4
+              ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
+    """X: uint16[S, H] bf16 bits -> (QX uint8[S, H/2 or H], SX uint8[S, K], B uint16[S, K] or None)."""
+    X = _c(X, np.uint16)
+    S, H = X.shape
+    K = H // G
+    QX = np.zeros((S, code_bytes_per_row(H, fmt)), np.uint8)
+    SX = np.zeros((S, K), np.uint8)
+    Lc = None if L is None else _c(L, np.int32)
+    B = None if L is None else np.zeros((S, K), np.uint16)
+    lib().orc_quant_act(_p(X), S, H, G, _p(Lc), fmt, _p(QX), _p(SX), _p(B))
+    return QX, SX, B
+
+
+def pack_weights(W: np.ndarray, G: int, L: Optional[np.ndarray], fmt: int = MXFP4
+                 ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
+    """W: uint16[N, H] bf16 bits -> (QW, SW uint8[N, K], WL uint16[N, K] or None)."""
+    W = _c(W, np.uint16)
+    N, H = W.shape
+    K = H // G
+    QW = np.zeros((N, code_bytes_per_row(H, fmt)), np.uint8)
+    SW = np.zeros((N, K), np.uint8)
+    Lc = None if L is None else _c(L, np.int32)
+    WL = None if L is None else np.zeros((N, K), np.uint16)
+    lib().orc_pack_weights(_p(W), N, H, G, _p(Lc), fmt, _p(QW), _p(SW), _p(WL))
+    return QW, SW, WL
+
+
+def gemm(QX, SX, QW, SW, G: int, B=None, WL=None, afmt: int = MXFP4, wfmt: int = MXFP4) -> np.ndarray:
+    """Dual-path GEMM in fp64 -> float64[S, N]."""
+    QX = _c(QX, np.uint8)
+    SX = _c(SX, np.uint8)
+    QW = _c(QW, np.uint8)
+    SW = _c(SW, np.uint8)
+    S = QX.shape[0]
+    N = QW.shape[0]
+    H = SX.shape[1] * G
+    assert QX.shape[1] == code_bytes_per_row(H, afmt) and QW.shape[1] == code_bytes_per_row(H, wfmt)
+    Bc = None if B is None else _c(B, np.uint16)
+    WLc = None if WL is None else _c(WL, np.uint16)
+    Y = np.zeros((S, N), np.float64)
+    lib().orc_gemm(_p(QX), _p(SX), afmt, _p(Bc), _p(QW), _p(SW), wfmt, _p(WLc), S, N, H, G, _p(Y))
+    return Y
+
+
+def build_table(Xcal: np.ndarray, G: int, alpha: float = 5.0, rho: float = 0.35):
+    """Algorithm 1 reading -> (L int32[K], hits int32[K], events int32[K])."""
+    Xcal = _c(Xcal, np.uint16)
+    R, H = Xcal.shape
+    K = H // G
+    L = np.zeros(K, np.int32)
+    hits = np.zeros(K, np.int32)
+    events = np.zeros(K, np.int32)
+    lib().orc_build_table(_p(Xcal), R, H, G, float(alpha), float(rho), _p(L), _p(hits), _p(events))
+    return L, hits, events
+
+
+def osc_linear(X, W, G: int, L, fmt: int = MXFP4):
+    """Convenience: quant_act + pack_weights + gemm (the whole OSC layer) in fp64."""
+    QX, SX, B = quant_act(X, G, L, fmt)
+    QW, SW, WL = pack_weights(W, G, L, MXFP4 if fmt == MXFP8 else fmt)
+    return gemm(QX, SX, QW, SW, G, B, WL, afmt=fmt, wfmt=MXFP4 if fmt == MXFP8 else fmt)

@@ -1,0 +1,276 @@
+/*
+ * CPU ORACLE for OSC W4A4 linear layers -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  It shares no source, header, table or helper with
+ * the HIP library; it is a plain, slow, obviously-correct restatement of what
+ * the OSC write-up computes, in fp64 wherever a value is not an integer code.
+ *
+ * Source: the web page "W4A4量化技术：OSC框架如何实现高效LLM部署" (OSC = Outlier
+ * Separation in Channel dimension):
+ *   §3.1  offline suppression table L (Algorithm 1; find_consistent_outlier
+ *         is named but not defined there -- reading in orc_build_table);
+ *   §3.2  before standard microscaling quantization, (1) zero the table-indexed
+ *         channel of each group after copying it into a 16-bit buffer B, and
+ *         (2) compute the scale on the zeroed tensor; the output is the sum of
+ *         a 4-bit path (Q_X ⊗ Q_W)·S and a 16-bit path B·W_L;
+ *   §3.3  the high-precision weight rows are pre-stored as one contiguous block;
+ *   §4    the W2 (down-projection) input switches to FP8 microscaling.
+ * Format details the page leaves to "standard microscaling": OCP Microscaling
+ * Formats (MX) v1.0 -- E8M0 shared scale X = 2^(floor(log2 amax) - emax_elem),
+ * emax_elem = 2 for E2M1 and 8 for E4M3; elements rounded to nearest, ties to
+ * even, saturating at the largest finite magnitude.
+ *
+ * Readings where the page is silent (each listed in the design notes):
+ *   - B and W_L are bf16 ("16bit" path; X and W are bf16, so B is a bit copy);
+ *   - table entries are offsets inside the group, -1 = no protected channel;
+ *   - an all-zero group gets scale exponent -127 (E8M0 code 0);
+ *   - a negative value that rounds to zero keeps its sign (code 0x8 / 0x80),
+ *     the zeroed slot itself is +0 (code 0x0);
+ *   - W is quantized unmodified (the zeroed activation slot multiplies it by 0);
+ *   - W_L is stored output-major: WL[n*K + k] = W[n, k*G + L[k]] (0 if L[k] = -1),
+ *     i.e. the K x N slice of the page kept in the same out x in layout as W;
+ *   - the FP8 fallback extracts nothing (no B, no W_L).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_MXFP4 0
+#define ORC_MXFP8 1
+
+/* ---------------------------------------------------------------- formats */
+
+/* bf16 is the upper half of an IEEE binary32. */
+double orc_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+ * Exponent field 0 encodes the subnormals 0 and 0.5. */
+double orc_e2m1_decode(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -mag : mag;
+}
+
+/* E4M3 (OCP "E4M3FN"): sign bit 7, exponent bits 6..3 (bias 7), mantissa 2..0.
+ * 0x7F / 0xFF are NaN; everything else is finite, max magnitude 448. */
+double orc_e4m3_decode(uint8_t code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* Round to the nearest representable magnitude among codes [0, ncodes),
+ * ties to the code with an even mantissa bit (codes are monotone in
+ * magnitude, so "even code" == "even mantissa"); values beyond the largest
+ * finite magnitude saturate to it. */
+static uint8_t nearest_code(double v, int ncodes, double (*decode)(uint8_t), int sign_shift) {
+  double m = fabs(v);
+  double top = decode((uint8_t)(ncodes - 1));
+  int best = ncodes - 1;
+  if (m < top) {
+    double bestd = INFINITY;
+    for (int c = 0; c < ncodes; ++c) {
+      double d = fabs(m - decode((uint8_t)c));
+      if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+        bestd = d;
+        best = c;
+      }
+    }
+  }
+  int neg = signbit(v) ? 1 : 0;
+  return (uint8_t)((neg << sign_shift) | best);
+}
+
+uint8_t orc_e2m1_encode(double v) { return nearest_code(v, 8, orc_e2m1_decode, 3); }
+uint8_t orc_e4m3_encode(double v) { return nearest_code(v, 127, orc_e4m3_decode, 7); }
+
+/* OCP MX shared exponent: floor(log2(amax)) - emax_elem, clamped to the E8M0
+ * range [-127, 127]; amax == 0 -> -127. */
+int orc_scale_exp(double amax, int fmt) {
+  int emax = (fmt == ORC_MXFP4) ? 2 : 8;
+  if (amax == 0.0) return -127;
+  int p;
+  frexp(amax, &p); /* amax = f * 2^p, f in [0.5, 1): floor(log2 amax) = p - 1 */
+  int e = (p - 1) - emax;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+static uint8_t encode_elem(double v, int fmt) {
+  return fmt == ORC_MXFP4 ? orc_e2m1_encode(v) : orc_e4m3_encode(v);
+}
+
+static double decode_elem(uint8_t c, int fmt) {
+  return fmt == ORC_MXFP4 ? orc_e2m1_decode(c) : orc_e4m3_decode(c);
+}
+
+/* Store element code i of a row: MXFP4 packs two per byte, element 2i in the
+ * low nibble; MXFP8 is one byte per element. */
+static void put_code(uint8_t* row, int i, uint8_t code, int fmt) {
+  if (fmt == ORC_MXFP8) {
+    row[i] = code;
+  } else if (i % 2 == 0) {
+    row[i / 2] = (uint8_t)((row[i / 2] & 0xF0) | code);
+  } else {
+    row[i / 2] = (uint8_t)((row[i / 2] & 0x0F) | (code << 4));
+  }
+}
+
+static uint8_t get_code(const uint8_t* row, int i, int fmt) {
+  if (fmt == ORC_MXFP8) return row[i];
+  return (i % 2 == 0) ? (row[i / 2] & 0x0F) : (row[i / 2] >> 4);
+}
+
+/* One row, one group: quantize vals[0..G) with the shared-exponent rule. */
+static void quant_group(const double* vals, int G, int fmt, uint8_t* qrow, int col0, uint8_t* scale_out) {
+  double amax = 0.0;
+  for (int j = 0; j < G; ++j)
+    if (fabs(vals[j]) > amax) amax = fabs(vals[j]);
+  int e = orc_scale_exp(amax, fmt);
+  *scale_out = (uint8_t)(e + 127);
+  for (int j = 0; j < G; ++j) put_code(qrow, col0 + j, encode_elem(ldexp(vals[j], -e), fmt), fmt);
+}
+
+/* --------------------------------------------------------- activations */
+
+/* §3.2: for each token s and group k with c = L[k] >= 0, copy X[s, kG+c] into
+ * B[s, k] and zero it; then microscaling-quantize the zeroed row.  With
+ * L == NULL (the FP8 fallback of §4, or direct MXFP4) nothing is extracted.
+ * X: S x H bf16 bits.  QX: S x H/2 bytes (MXFP4) or S x H (MXFP8).
+ * SX: S x K E8M0 codes.  B: S x K bf16 bits (ignored when L == NULL). */
+void orc_quant_act(const uint16_t* X, int S, int H, int G, const int32_t* L, int fmt,
+                   uint8_t* QX, uint8_t* SX, uint16_t* B) {
+  int K = H / G;
+  long qstride = (fmt == ORC_MXFP4) ? H / 2 : H;
+#pragma omp parallel for schedule(static)
+  for (int s = 0; s < S; ++s) {
+    double vals[256];
+    for (int k = 0; k < K; ++k) {
+      for (int j = 0; j < G; ++j) vals[j] = orc_bf16_value(X[(long)s * H + k * G + j]);
+      if (L) {
+        int c = L[k];
+        if (c >= 0) {
+          B[(long)s * K + k] = X[(long)s * H + k * G + c]; /* bit copy, sign and -0 included */
+          vals[c] = 0.0;                                  /* +0 */
+        } else {
+          B[(long)s * K + k] = 0;
+        }
+      }
+      quant_group(vals, G, fmt, QX + s * qstride, k * G, SX + (long)s * K + k);
+    }
+  }
+}
+
+/* -------------------------------------------------------------- weights */
+
+/* §3.2-§3.3 weight side: W (N x H bf16, PyTorch out x in) is microscaling-
+ * quantized along H, unmodified; W_L gathers the indexed channels' weights
+ * into a dense contiguous block, WL[n*K + k] = W[n, kG + L[k]] (0 if -1). */
+void orc_pack_weights(const uint16_t* W, int N, int H, int G, const int32_t* L, int fmt,
+                      uint8_t* QW, uint8_t* SW, uint16_t* WL) {
+  int K = H / G;
+  long qstride = (fmt == ORC_MXFP4) ? H / 2 : H;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    double vals[256];
+    for (int k = 0; k < K; ++k) {
+      for (int j = 0; j < G; ++j) vals[j] = orc_bf16_value(W[(long)n * H + k * G + j]);
+      quant_group(vals, G, fmt, QW + n * qstride, k * G, SW + (long)n * K + k);
+      if (L && WL) WL[(long)n * K + k] = (L[k] >= 0) ? W[(long)n * H + k * G + L[k]] : 0;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ GEMM */
+
+/* §3.2 dual path: Y[s, n] = sum_k 2^(eX[s,k] + eW[n,k]) * sum_{j<G} q(X)[s,kG+j] * q(W)[n,kG+j]
+ *                         + sum_k B[s, k] * WL[n, k]
+ * in fp64 (every product of two decoded codes, and of two bf16 values, is
+ * exact in fp64).  B / WL may be NULL: no compensation path (plain MX GEMM,
+ * and the FP8 fallback of §4).  afmt / wfmt: element format of each side. */
+void orc_gemm(const uint8_t* QX, const uint8_t* SX, int afmt, const uint16_t* B,
+              const uint8_t* QW, const uint8_t* SW, int wfmt, const uint16_t* WL,
+              int S, int N, int H, int G, double* Y) {
+  int K = H / G;
+  long xstride = (afmt == ORC_MXFP4) ? H / 2 : H;
+  long wstride = (wfmt == ORC_MXFP4) ? H / 2 : H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int s = 0; s < S; ++s) {
+    for (int n = 0; n < N; ++n) {
+      double y = 0.0;
+      for (int k = 0; k < K; ++k) {
+        double part = 0.0;
+        for (int j = 0; j < G; ++j)
+          part += decode_elem(get_code(QX + s * xstride, k * G + j, afmt), afmt) *
+                  decode_elem(get_code(QW + n * wstride, k * G + j, wfmt), wfmt);
+        y += ldexp(part, ((int)SX[(long)s * K + k] - 127) + ((int)SW[(long)n * K + k] - 127));
+      }
+      if (B && WL)
+        for (int k = 0; k < K; ++k)
+          y += orc_bf16_value(B[(long)s * K + k]) * orc_bf16_value(WL[(long)n * K + k]);
+      Y[(long)s * N + n] = y;
+    }
+  }
+}
+
+/* ------------------------------------------------------- table builder */
+
+/* §3.1 Algorithm 1 for one (position, layer): for every group k of the R x H
+ * calibration activations, L[k] = find_consistent_outlier(X[:, kG:(k+1)G], alpha)
+ * or -1.  The page names find_consistent_outlier without defining it; reading:
+ *   - a row is an outlier event when its largest |x| exceeds alpha times the
+ *     group's mean |x| (alpha = 5 by default, §3.1 / §5.2); the event's channel
+ *     is that row's arg-max (lowest index on ties);
+ *   - the candidate j* is the most frequent event channel (lowest on ties);
+ *   - it is "consistent" (token persistence, §1 / §2.1) when it is the event
+ *     channel on at least rho of all R calibration tokens (rho = 0.35, the
+ *     35% boundary of §2.3); otherwise, or with no events at all, L[k] = -1.
+ * hits[k] = events whose channel is j* (N_k^hit of §2.2), events[k] = all
+ * events (N_k^total), so C_k = hits / events is the page's clustering density.
+ * Returns the number of protected groups. */
+int orc_build_table(const uint16_t* Xcal, int R, int H, int G, double alpha, double rho,
+                    int32_t* L, int32_t* hits, int32_t* events) {
+  int K = H / G;
+  int protected_groups = 0;
+  for (int k = 0; k < K; ++k) {
+    long hist[256];
+    for (int j = 0; j < G; ++j) hist[j] = 0;
+    long nev = 0;
+    for (int r = 0; r < R; ++r) {
+      double m = -1.0, sum = 0.0;
+      int jr = 0;
+      for (int j = 0; j < G; ++j) {
+        double a = fabs(orc_bf16_value(Xcal[(long)r * H + k * G + j]));
+        sum += a;
+        if (a > m) {
+          m = a;
+          jr = j;
+        }
+      }
+      double mean = sum / G;
+      if (m > alpha * mean) {
+        hist[jr] += 1;
+        nev += 1;
+      }
+    }
+    int jstar = 0;
+    for (int j = 1; j < G; ++j)
+      if (hist[j] > hist[jstar]) jstar = j;
+    hits[k] = (int32_t)(nev ? hist[jstar] : 0);
+    events[k] = (int32_t)nev;
+    if (nev > 0 && (double)hist[jstar] >= rho * (double)R) {
+      L[k] = jstar;
+      ++protected_groups;
+    } else {
+      L[k] = -1;
+    }
+  }
+  return protected_groups;
+}
