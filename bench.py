@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the OSC W4A4 linear-layer hot path on one MI355X.
+
+One step = one pass of the online path over a batch of synthetic activations:
+osc_quant_act (outlier extraction into B + zeroing + E8M0 scale + E2M1 encode) followed
+by osc_gemm (scaled-MFMA MXFP4 main path with the bf16 compensation B·W_L fused into the
+same accumulators), on the Qwen3-8B QKV projection shape S=2048, H=4096, N=6144, G=32
+(OSC page "W4A4量化技术：OSC框架如何实现高效LLM部署", §3.2).  Weight preparation is
+offline (§3.3) and untimed.  Inputs are resident in HBM before the timed region; the
+steps rotate over buffer sets whose total exceeds the 256 MB Infinity Cache.
+
+metric: TFLOP/s = 2*S*H*N / (t_quant + t_gemm), from the wall clock of K steps
+bracketed by device synchronisation.  The GEMM's average kernel duration is measured
+with HIP events on the stream the kernels run on, for the roofline object.  The CPU
+baseline is the oracle (test infrastructure) timed on a bounded row sample.
+
+Prints ONE JSON line.  Extra per-workload rows (FFN prefill / decode, W2 FP8 fallback,
+group-size sweep) go under "rows".
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}  # MI355X dense, published
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-rows", action="store_true", help="skip the extra workload rows")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--only", default=None, help="time only this workload row (profiling runs)")
+    return p.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "w4a4_outlier_split_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Layer:
+    """Device buffers of one OSC linear layer (one buffer set)."""
+
+    def __init__(self, torch, osc, w, L, afmt, wfmt, dev, X_dev=None, packed=None):
+        S, H, N, G = w.S, w.H, w.N, w.G
+        K = H // G
+        self.S, self.H, self.N, self.G, self.L, self.afmt, self.wfmt = S, H, N, G, L, afmt, wfmt
+        cq = lambda n, f: (n, H // 2 if f == osc.OSC_MXFP4 else H)
+        import numpy as np
+        self.X = X_dev if X_dev is not None else torch.from_numpy(w.X.view(np.int16)).to(dev)
+        self.QX = torch.empty(cq(S, afmt), dtype=torch.uint8, device=dev)
+        self.SX = torch.empty((S, K), dtype=torch.uint8, device=dev)
+        self.B = torch.empty((S, K), dtype=torch.int16, device=dev) if L is not None else None
+        if packed is None:
+            Wd = torch.from_numpy(w.W.view(np.int16)).to(dev)
+            self.QW = torch.empty(cq(N, wfmt), dtype=torch.uint8, device=dev)
+            self.SW = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            self.WL = torch.empty((N, K), dtype=torch.int16, device=dev) if L is not None else None
+            osc.osc_pack_weights(Wd, N, H, G, L, wfmt, self.QW, self.SW, self.WL)  # offline, untimed
+            del Wd
+        else:
+            self.QW, self.SW, self.WL = (t.clone() if t is not None else None for t in packed)
+        self.Y = torch.empty((S, N), dtype=torch.bfloat16, device=dev)
+        p = lambda t: None if t is None else t.data_ptr()
+        self.ptr = {k: p(getattr(self, k)) for k in ("X", "QX", "SX", "B", "QW", "SW", "WL", "Y")}
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in (self.X, self.QX, self.SX, self.B, self.QW, self.SW,
+                                                          self.WL, self.Y) if t is not None)
+
+
+def time_layer(torch, osc, sets, steps, warmup, stream):
+    """Run quant + GEMM over rotating buffer sets.  Returns wall seconds per step and the
+    average event-timed durations of the quant and GEMM kernels inside the timed region."""
+    s = stream.cuda_stream
+
+    def quant(l):
+        P = l.ptr
+        osc.osc_quant_act(P["X"], l.S, l.H, l.G, l.L, l.afmt, P["QX"], P["SX"], P["B"], s)
+
+    def gemm(l):
+        P = l.ptr
+        if l.afmt == osc.OSC_MXFP4:
+            osc.osc_gemm(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, P["Y"],
+                         osc.OSC_Y_BF16, s)
+        else:
+            osc.osc_gemm_fp8(P["QX"], P["SX"], P["QW"], P["SW"], l.wfmt, l.S, l.N, l.H, l.G, P["Y"],
+                             osc.OSC_Y_BF16, s)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            l = sets[i % len(sets)]
+            quant(l)
+            gemm(l)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            l = sets[i % len(sets)]
+            ev[3 * i].record(stream)
+            quant(l)
+            ev[3 * i + 1].record(stream)
+            gemm(l)
+            ev[3 * i + 2].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    tq = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps * 1e-3
+    tg = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps * 1e-3
+    return (t1 - t0) / steps, tq, tg
+
+
+def make_sets(torch, osc, w, L, afmt, wfmt, dev):
+    first = Layer(torch, osc, w, L, afmt, wfmt, dev)
+    sets = [first]
+    per = first.nbytes()
+    nsets = max(2, min(16, -(-(MALL_BYTES * 5 // 4) // per)))
+    for _ in range(nsets - 1):
+        sets.append(Layer(torch, osc, w, L, afmt, wfmt, dev, X_dev=first.X.clone(),
+                          packed=(first.QW, first.SW, first.WL)))
+    return sets
+
+
+def gemm_bytes(w, afmt, wfmt, comp):
+    """Algorithmic HBM bytes of one GEMM launch: every operand read once, Y (bf16) written once."""
+    S, H, N, G = w.S, w.H, w.N, w.G
+    K = H // G
+    cb = lambda f: 0.5 if f == 0 else 1.0
+    b = S * H * cb(afmt) + S * K + N * H * cb(wfmt) + N * K + 2 * S * N
+    if comp:
+        b += 2 * S * K + 2 * N * K
+    return b
+
+
+def quant_bytes(w, afmt, extract):
+    S, H, G = w.S, w.H, w.G
+    K = H // G
+    return 2 * S * H + S * H * (0.5 if afmt == 0 else 1.0) + S * K + (2 * S * K if extract else 0)
+
+
+def table_on_gpu(torch, osc, w, G, dev):
+    import numpy as np
+    K = w.H // G
+    out = [torch.empty((K,), dtype=torch.int32, device=dev) for _ in range(3)]
+    cal = torch.from_numpy(w.calib.view(np.int16)).to(dev)
+    osc.osc_build_table(cal, cal.shape[0], w.H, G, 5.0, 0.35, *out)
+    torch.cuda.synchronize()
+    return out[0].cpu().numpy()
+
+
+def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup):
+    sets = make_sets(torch, osc, w, L, afmt, wfmt, dev)
+    wall, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
+    flops = 2.0 * w.S * w.H * w.N
+    comp = L is not None
+    row = {"workload": name, "S": w.S, "H": w.H, "N": w.N, "G": w.G,
+           "path": ("osc_mxfp4" if afmt == 0 else ("w8a4_fp8" if wfmt == 0 else "w8a8_fp8")),
+           "protected_groups": None if L is None else int((L >= 0).sum()),
+           "buffer_sets": len(sets), "ms_per_step": wall * 1e3,
+           "tflops": flops / wall / 1e12, "t_quant_us": tq * 1e6, "t_gemm_us": tg * 1e6,
+           "gemm_tflops": flops / tg / 1e12,
+           "quant_gbs": quant_bytes(w, afmt, comp) / tq / 1e9,
+           "gemm_gbs": gemm_bytes(w, afmt, wfmt, comp) / tg / 1e9}
+    peak = PEAK_TFLOPS["mxfp4"] if afmt == 0 else PEAK_TFLOPS["fp8"]
+    row["gemm_frac_of_peak"] = row["gemm_tflops"] / peak
+    row["frac_of_mxfp4_peak"] = row["tflops"] / PEAK_TFLOPS["mxfp4"]
+    del sets
+    torch.cuda.empty_cache()
+    return row
+
+
+def cpu_baseline(w, L, target_s):
+    """The oracle (quant + dual-path GEMM, fp64) on the first rows of the same workload,
+    grown until the sample costs about target_s seconds of CPU time."""
+    import oracle
+    QW, SW, WL = oracle.pack_weights(w.W, w.G, L)  # offline weight side, untimed as on the GPU
+    rows = 1
+    while True:
+        t0 = time.perf_counter()
+        QX, SX, B = oracle.quant_act(w.X[:rows], w.G, L)
+        oracle.gemm(QX, SX, QW, SW, w.G, B, WL)
+        el = time.perf_counter() - t0
+        if el >= target_s or rows >= w.S:
+            break
+        rows = min(w.S, max(rows + 1, int(rows * target_s / max(el, 1e-3) * 1.05)))
+    flops = 2.0 * rows * w.H * w.N
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {rows} of {w.S} token rows, all N={w.N} outputs: quantization with extraction "
+                      f"+ dual-path GEMM in fp64 ({el:.1f} s); weight packing untimed",
+            "seconds": el}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the OSC layer's one-GPU share is the workload; "
+              f"--gpus {args.gpus} is not supported (sharding is described in DESIGN.md, not run)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+    import w4a4_outlier_split_amd as osc
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    t_start = time.perf_counter()
+
+    # ---- the headline workload: Qwen3-8B QKV projection
+    w = synth.qkv(S=2048)
+    L = table_on_gpu(torch, osc, w, w.G, dev)
+    rows = []
+    head = None
+    if args.only in (None, "qkv"):
+        head = run_row(torch, osc, "qkv_proj_s2048_g32", w, L, osc.OSC_MXFP4, osc.OSC_MXFP4, dev, stream,
+                       args.steps, args.warmup)
+
+    # ---- more rows of the same path at the other configurations
+    if not args.no_rows:
+        def want(n):
+            return args.only is None or args.only == n
+        if want("ffn_up_s4096") or want("ffn_up_s16"):
+            wf = synth.ffn_up(S=4096)
+            Lf = table_on_gpu(torch, osc, wf, 32, dev)
+            if want("ffn_up_s4096"):
+                rows.append(run_row(torch, osc, "ffn_up_s4096_g32", wf, Lf, 0, 0, dev, stream, 50, 10))
+            if want("ffn_up_s16"):
+                wd = synth.ffn_up(S=16)
+                r = run_row(torch, osc, "ffn_up_s16_g32_decode", wd, Lf, 0, 0, dev, stream, 200, 20)
+                r["gemm_frac_of_hbm"] = r["gemm_gbs"] / PEAK_HBM_GBS
+                rows.append(r)
+            del wf
+        if want("ffn_down_fp8") or want("ffn_down_osc"):
+            wdn = synth.ffn_down(S=4096)
+            if want("ffn_down_fp8"):
+                rows.append(run_row(torch, osc, "ffn_down_s4096_fp8_w4a8", wdn, None, 1, 0, dev, stream, 50, 10))
+            if want("ffn_down_osc"):
+                Ld = table_on_gpu(torch, osc, wdn, 32, dev)
+                rows.append(run_row(torch, osc, "ffn_down_s4096_forced_osc", wdn, Ld, 0, 0, dev, stream, 50, 10))
+            del wdn
+        for S in (8192, 16):
+            for G in (16, 32, 64):
+                n = f"gsweep_s{S}_g{G}"
+                if not want(n) and not want("gsweep"):
+                    continue
+                ws = synth.group_sweep(S, G)
+                Ls = table_on_gpu(torch, osc, ws, G, dev)
+                r = run_row(torch, osc, n, ws, Ls, 0, 0, dev, stream, 50 if S > 16 else 200, 10)
+                if S == 16:
+                    r["gemm_frac_of_hbm"] = r["gemm_gbs"] / PEAK_HBM_GBS
+                rows.append(r)
+
+    if head is None:
+        print(json.dumps({"rows": rows}))
+        return
+
+    # ---- roofline of the dominant kernel (the GEMM, MFMA-bound)
+    gemm_flops = 2.0 * w.S * w.H * w.N
+    achieved = gemm_flops / (head["t_gemm_us"] * 1e-6) / 1e12
+    traffic = None
+    tf_path = os.path.join(ROOT, "profiles", "gemm_mxfp4_qkv_s2048_traffic.json")
+    if os.path.exists(tf_path):
+        with open(tf_path) as f:
+            tf = json.load(f)
+        if tf.get("source_hash") == src_hash("osc_gemm.hip"):
+            traffic = tf.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["mxfp4"], "unit": "TFLOP/s",
+                "frac": achieved / PEAK_TFLOPS["mxfp4"], "traffic": traffic,
+                "kernel": "k_gemm (osc_gemm, MXFP4 scaled MFMA + fused bf16 compensation)",
+                "flops_per_launch": gemm_flops, "avg_launch_us": head["t_gemm_us"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, L, args.cpu_seconds)
+
+    ms = head["ms_per_step"]
+    out = {
+        "metric": "fused OSC W4A4 quant+GEMM TFLOP/s at Qwen3-8B shapes; % of MXFP4 MFMA peak",
+        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": "Qwen3-8B QKV projection, one OSC W4A4 linear layer: S=2048 tokens, H=4096, "
+                               "N=6144, G=32", "S": w.S, "H": w.H, "N": w.N, "G": w.G,
+                   "protected_groups": head["protected_groups"], "K": w.H // w.G,
+                   "table": "built on the GPU (osc_build_table) from 1536 seeded calibration rows"},
+        "frac_of_mxfp4_peak": head["tflops"] / PEAK_TFLOPS["mxfp4"],
+        "t_quant_us": head["t_quant_us"], "t_gemm_us": head["t_gemm_us"],
+        "roofline": roofline,
+        "quant_roofline": {"bound": "hbm", "achieved": head["quant_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": head["quant_gbs"] / PEAK_HBM_GBS},
+        "cpu_baseline": cpu,
+        "rows": rows,
+        "bench_seconds": time.perf_counter() - t_start,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * osc.h -- C ABI of the OSC W4A4 linear-layer library for MI355X (gfx950).
+ *
+ * OSC (Outlier Separation in Channel dimension), as described on the page
+ * "W4A4量化技术：OSC框架如何实现高效LLM部署":
+ *   §3.1  an offline table L gives, per group k of G input channels, the offset of
+ *         the one channel that persistently carries outliers (-1 = none);
+ *   §3.2  online, that channel is copied into a dense 16-bit buffer B (S x K) and
+ *         zeroed, the zeroed activations are microscaling-quantized with a scale
+ *         computed after zeroing, and the layer output is the sum of a 4-bit path
+ *         and a 16-bit path:  Y = (Q_X ⊗ Q_W)·S + B·W_L;
+ *   §3.3  the 16-bit weight slice W_L is prepared offline as one contiguous block;
+ *   §4    the down-projection (W2) input switches to FP8 microscaling instead.
+ * Formats ("standard microscaling", OCP MX v1.0): one E8M0 scale byte per group,
+ * 2^(floor(log2 amax) - emax) with emax = 2 (E2M1) or 8 (E4M3), clamped to
+ * [-127, 127] (an all-zero group gets code 0); elements rounded to nearest,
+ * ties to even, saturating (E2M1: +-6, E4M3: +-448); a negative value that
+ * rounds to zero keeps its sign bit; the zeroed outlier slot encodes as +0.
+ *
+ * Conventions shared by every call
+ *   - bf16 tensors are raw IEEE bfloat16; all matrices are row-major, no padding.
+ *   - X is S x H (tokens x input channels); W is N x H (PyTorch Linear: out x in).
+ *   - K = H / G groups per row; group k covers channels [k*G, (k+1)*G).
+ *   - Element codes: MXFP4 packs two E2M1 codes per byte, element 2i in the low
+ *     nibble of byte i (H/2 bytes per row); MXFP8 stores one E4M3 byte per element.
+ *   - Scales: rows x K bytes of E8M0 (bias 127; 255 is never produced).
+ *   - L: HOST array of K int32 entries in {-1} ∪ [0, G), read during the call and
+ *     passed to the kernels by value (kernel arguments), so a call can be captured
+ *     in a HIP graph; K <= OSC_MAX_GROUPS.
+ *   - Every other pointer is DEVICE memory owned by the caller, 16-byte aligned.
+ *     The library never allocates, frees or synchronizes and keeps no pointer
+ *     after returning.  Outputs must not alias inputs.
+ *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued on it; results are ready when the stream has drained.
+ *   - Validation happens on the host, before any HIP call: a call that returns an
+ *     error status launched nothing.  OSC_E_DEVICE means a launch was rejected by
+ *     the runtime; faults inside a kernel surface at the caller's next sync.
+ *   - Inputs must be finite (NaN / Inf in X or W is outside the contract).
+ *   - S == 0 (or N == 0) is valid: after the size / format checks the call returns
+ *     OSC_OK without inspecting pointers or launching anything.
+ *   - Calls on different streams are independent; the library is thread-safe.
+ */
+#ifndef OSC_H
+#define OSC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OSC_OK = 0,
+  OSC_E_NULL = 1,   /* a required pointer is NULL (or a pointer that must be NULL is not) */
+  OSC_E_SHAPE = 2,  /* a size or the group size violates the constraints of the call    */
+  OSC_E_TABLE = 3,  /* a table entry is outside {-1} ∪ [0, G)                            */
+  OSC_E_ALIGN = 4,  /* a device pointer is not 16-byte aligned                           */
+  OSC_E_FORMAT = 5, /* unknown format or output type, or an unsupported combination     */
+  OSC_E_DEVICE = 6  /* the HIP runtime rejected a kernel launch                          */
+} osc_status;
+
+typedef enum {
+  OSC_MXFP4 = 0, /* E2M1 elements + E8M0 group scale */
+  OSC_MXFP8 = 1  /* E4M3 elements + E8M0 group scale */
+} osc_fmt;
+
+typedef enum {
+  OSC_Y_BF16 = 0, /* output rounded to bfloat16 (nearest, ties to even) */
+  OSC_Y_F32 = 1   /* output kept in fp32 */
+} osc_ytype;
+
+#define OSC_MAX_GROUPS 1024
+
+/*
+ * osc_pack_weights -- offline weight preparation (§3.2 weight side, §3.3).
+ *   W   [N][H] bf16, device.  Quantized unmodified along H in groups of G.
+ *   L   host int32[K] table slice, or NULL (no compensation path: WL must be NULL).
+ *   wfmt  OSC_MXFP4 or OSC_MXFP8.
+ *   QW  [N][H/2] bytes (MXFP4) or [N][H] (MXFP8), device, written.
+ *   SW  [N][K] E8M0 bytes, device, written.
+ *   WL  [N][K] bf16, device, written: WL[n][k] = W[n][k*G + L[k]], or +0 when
+ *       L[k] = -1.  This is the page's K x N slice W_L stored output-major (the
+ *       layout of W itself), so every output channel's K compensation weights
+ *       are contiguous.
+ * Constraints: N >= 0, H > 0, G in {16, 32, 64}, H % G == 0, K <= OSC_MAX_GROUPS.
+ */
+osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt,
+                            void* QW, uint8_t* SW, void* WL, void* stream);
+
+/*
+ * osc_quant_act -- online activation quantization with outlier extraction (§3.2).
+ *   X   [S][H] bf16, device, read only (zeroing is logical).
+ *   L   host int32[K] table slice, or NULL: no extraction (direct MX quantization,
+ *       and the FP8 fallback of §4); then B must be NULL.
+ *   afmt  OSC_MXFP4 or OSC_MXFP8.
+ *   QX  [S][H/2] (MXFP4) or [S][H] (MXFP8) bytes, device, written.
+ *   SX  [S][K] E8M0 bytes, device, written; computed on the zeroed group.
+ *   B   [S][K] bf16, device, written: B[s][k] = X[s][k*G + L[k]] bit for bit, or
+ *       +0 when L[k] = -1.
+ * Constraints: S >= 0, H > 0, G in {16, 32, 64}, H % G == 0, K <= OSC_MAX_GROUPS.
+ */
+osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt,
+                         void* QX, uint8_t* SX, void* B, void* stream);
+
+/*
+ * osc_gemm -- the dual-path OSC product (§3.2):
+ *   Y[s][n] = sum_k 2^(eX[s][k] + eW[n][k]) * sum_{j<G} qX[s][kG+j] * qW[n][kG+j]
+ *           + sum_k B[s][k] * WL[n][k]
+ * with MXFP4 operands from osc_quant_act / osc_pack_weights, accumulated in
+ * fp32 (each 4-bit product and each bf16 product is exact in fp32).  The 16-bit
+ * compensation runs in the same kernel, into the same fp32 accumulators.
+ *   B, WL  both NULL for a plain MXFP4 GEMM (no compensation), else both set.
+ *   Y   [S][N], bf16 or fp32 per yt, device, written.
+ * Constraints: S >= 0, N >= 0, G in {16, 32, 64}, H % 256 == 0, K <= OSC_MAX_GROUPS,
+ * and with compensation K % 8 == 0.
+ */
+osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void* QW,
+                    const uint8_t* SW, const void* WL, int S, int N, int H, int G, void* Y,
+                    osc_ytype yt, void* stream);
+
+/*
+ * osc_gemm_fp8 -- the W2 fallback of §4: Y = (QX8 ⊗ QW)·S with E4M3 activations
+ * (osc_quant_act with afmt = OSC_MXFP8, L = NULL) and weights in wfmt (OSC_MXFP4,
+ * the default W4A8 reading, or OSC_MXFP8); no extraction, no compensation.
+ *   Y   [S][N], bf16 or fp32 per yt, device, written.
+ * Constraints: S >= 0, N >= 0, G in {32, 64}, H % 256 == 0, K <= OSC_MAX_GROUPS.
+ */
+osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, const uint8_t* SW,
+                        osc_fmt wfmt, int S, int N, int H, int G, void* Y, osc_ytype yt,
+                        void* stream);
+
+/*
+ * osc_build_table -- offline suppression-table slice for one (position, layer)
+ * (§3.1, Algorithm 1), from R calibration rows Xcal [R][H] bf16 (device).
+ * find_consistent_outlier is only named on the page; this library reads it as:
+ * a row is an outlier event in group k when the group's largest |x| exceeds
+ * alpha times the group's mean |x| (compared in fp64), its channel being the
+ * lowest arg-max; the group's candidate is its most frequent event channel
+ * (lowest on ties), kept when it is the event channel on at least rho * R rows.
+ *   L, hits, events  device int32[K], written: the entry (-1 = none), the
+ *   candidate's event count and all events (hits / events is the page's
+ *   clustering density C_k, §2.2).
+ * Constraints: R > 0, H > 0, G in {16, 32, 64}, H % G == 0, K <= OSC_MAX_GROUPS,
+ * alpha > 0, 0 < rho <= 1.
+ */
+osc_status osc_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho,
+                           int32_t* L, int32_t* hits, int32_t* events, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* osc_status_str(osc_status s);
+
+/* The HIP runtime's description of the error behind the calling thread's most
+ * recent OSC_E_DEVICE ("no device error" if there was none); static storage. */
+const char* osc_last_device_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSC_H */

@@ -51,6 +51,8 @@ def lib():
         L.orc_gemm.restype = None
         L.orc_build_table.argtypes = [P, i, i, i, ctypes.c_double, ctypes.c_double, P, P, P]
         L.orc_build_table.restype = i
+        L.orc_threads.argtypes = []
+        L.orc_threads.restype = i
         _lib = L
     return _lib
 
@@ -61,6 +63,11 @@ def _p(a: Optional[np.ndarray]):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_threads())
 
 
 # ------------------------------------------------------------ scalar codecs

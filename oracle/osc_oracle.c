@@ -33,11 +33,15 @@
  *   - the FP8 fallback extracts nothing (no B, no W_L).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
 #define ORC_MXFP4 0
 #define ORC_MXFP8 1
+
+/* Threads an OpenMP region of this library uses (for reporting the CPU baseline). */
+int orc_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- formats */
 

@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: libosc loads, exports every function include/osc.h declares,
+and rejects invalid arguments with the documented status before any HIP call (so no
+kernel is launched and no pointer is dereferenced; the fake addresses below are never
+touched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "osc.h")
+
+osc = pytest.importorskip("w4a4_outlier_split_amd", reason="libosc.so not built")
+
+A = 0x10000  # 16-byte aligned fake device address (never dereferenced by a rejected call)
+U = 0x10008  # misaligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:osc_status|const char\*)\s+(osc_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(osc.EXPORTS)
+    lib = ctypes.CDLL(osc.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in osc.STATUS.items():
+        assert osc.osc_status_str(code).startswith(name)
+
+
+def status(fn, *args):
+    r = getattr(osc._lib, fn)(*args)
+    return r
+
+
+def L8(vals):
+    arr = np.asarray(vals, np.int32)
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_quant_act_validation():
+    keep, lp = L8([-1] * 8)
+    q = lambda X=A, S=16, H=256, G=32, l=lp, f=0, QX=A, SX=A, B=A: status("osc_quant_act", X, S, H, G, l, f, QX, SX, B, None)
+    assert q(f=7) == 5                      # bad format
+    assert q(G=8) == 2 and q(G=128) == 2     # G not in {16, 32, 64}
+    assert q(H=250) == 2                     # H % G != 0
+    assert q(S=-1) == 2
+    assert q(X=None) == 1 and q(QX=None) == 1 and q(SX=None) == 1
+    assert q(B=None) == 1                    # table given but no B
+    assert q(l=None) == 1                    # B given but no table
+    assert q(X=U) == 4 and q(B=U) == 4
+    bad, bp = L8([0, 1, 2, 32, -1, -1, -1, -1])
+    assert q(l=bp) == 3                      # entry >= G
+    bad2, bp2 = L8([0, -2, 0, 0, 0, 0, 0, 0])
+    assert q(l=bp2) == 3
+    assert q(H=1024 * 64 + 64, G=64, l=None, B=None) == 2  # K > OSC_MAX_GROUPS
+
+
+def test_pack_weights_validation():
+    keep, lp = L8([3] * 8)
+    p = lambda W=A, N=128, H=256, G=32, l=lp, f=0, QW=A, SW=A, WL=A: status("osc_pack_weights", W, N, H, G, l, f, QW, SW, WL, None)
+    assert p(f=2) == 5
+    assert p(WL=None) == 1 and p(l=None) == 1
+    assert p(W=U) == 4 and p(SW=U) == 4
+    assert p(N=-3) == 2
+    bad, bp = L8([3, 3, 3, 3, 3, 3, 3, 40])
+    assert p(l=bp) == 3
+
+
+def test_gemm_validation():
+    g = lambda QX=A, SX=A, B=A, QW=A, SW=A, WL=A, S=16, N=128, H=256, G=32, Y=A, yt=0: status(
+        "osc_gemm", QX, SX, B, QW, SW, WL, S, N, H, G, Y, yt, None)
+    assert g(yt=3) == 5
+    assert g(H=384) == 2                     # H % 256 != 0
+    assert g(H=256, G=64) == 2               # K = 4: compensation needs K % 8 == 0
+    assert g(B=None) == 1 and g(WL=None) == 1
+    assert g(Y=None) == 1
+    assert g(Y=U) == 4 and g(WL=U) == 4
+    assert g(S=-1) == 2 and g(N=-1) == 2
+    assert g(S=0) == 0 and g(N=0) == 0       # valid, nothing launched
+
+
+def test_gemm_fp8_validation():
+    f = lambda QX=A, SX=A, QW=A, SW=A, wf=0, S=16, N=128, H=256, G=32, Y=A, yt=0: status(
+        "osc_gemm_fp8", QX, SX, QW, SW, wf, S, N, H, G, Y, yt, None)
+    assert f(wf=9) == 5
+    assert f(G=16) == 2
+    assert f(QW=None) == 1
+    assert f(SX=U) == 4
+    assert f(S=0) == 0
+
+
+def test_build_table_validation():
+    b = lambda X=A, R=1536, H=256, G=32, al=5.0, rho=0.35, L=A, hi=A, ev=A: status(
+        "osc_build_table", X, R, H, G, ctypes.c_double(al), ctypes.c_double(rho), L, hi, ev, None)
+    assert b(R=0) == 2
+    assert b(al=0.0) == 2 and b(rho=0.0) == 2 and b(rho=1.5) == 2
+    assert b(L=None) == 1
+    assert b(X=U) == 4

@@ -1,0 +1,145 @@
+// C ABI of libosc: argument validation (host only, before any HIP call) and kernel dispatch.
+// The operations are those of the OSC page "W4A4量化技术：OSC框架如何实现高效LLM部署":
+// §3.1 table (osc_build_table), §3.2 extraction + microscaling quantization (osc_quant_act),
+// §3.2-§3.3 offline weight preparation (osc_pack_weights), §3.2 dual-path GEMM (osc_gemm),
+// §4 FP8 fallback (osc_gemm_fp8).
+#include <stdint.h>
+
+#include "osc_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_g(int G) { return G == 16 || G == 32 || G == 64; }
+
+osc_status check_dims(int rows, int H, int G) {
+  if (rows < 0 || H <= 0 || !valid_g(G) || H % G != 0) return OSC_E_SHAPE;
+  if (H / G > OSC_MAX_GROUPS) return OSC_E_SHAPE;
+  return OSC_OK;
+}
+
+// copy the host table slice into the kernel-argument struct, checking every entry
+osc_status pack_table(const int32_t* L, int K, int G, osc::TableArg* t) {
+  for (int k = 0; k < K; ++k) {
+    const int32_t v = L[k];
+    if (v < -1 || v >= G) return OSC_E_TABLE;
+    t->v[k] = (int8_t)v;
+  }
+  for (int k = K; k < OSC_MAX_GROUPS; ++k) t->v[k] = -1;
+  return OSC_OK;
+}
+
+// the HIP error behind the calling thread's most recent OSC_E_DEVICE
+thread_local hipError_t g_last_error = hipSuccess;
+
+osc_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return OSC_OK;
+  g_last_error = e;
+  return OSC_E_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* osc_status_str(osc_status s) {
+  switch (s) {
+    case OSC_OK: return "OSC_OK";
+    case OSC_E_NULL: return "OSC_E_NULL: a required pointer is NULL (or a pointer that must be NULL is not)";
+    case OSC_E_SHAPE: return "OSC_E_SHAPE: a size or the group size violates the constraints of the call";
+    case OSC_E_TABLE: return "OSC_E_TABLE: a table entry is outside {-1} U [0, G)";
+    case OSC_E_ALIGN: return "OSC_E_ALIGN: a device pointer is not 16-byte aligned";
+    case OSC_E_FORMAT: return "OSC_E_FORMAT: unknown or unsupported format / output type";
+    case OSC_E_DEVICE: return "OSC_E_DEVICE: the HIP runtime rejected a kernel launch";
+  }
+  return "unknown osc_status";
+}
+
+const char* osc_last_device_error(void) {
+  return g_last_error == hipSuccess ? "no device error" : hipGetErrorString(g_last_error);
+}
+
+osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt, void* QX, uint8_t* SX,
+                         void* B, void* stream) {
+  if (afmt != OSC_MXFP4 && afmt != OSC_MXFP8) return OSC_E_FORMAT;
+  osc_status st = check_dims(S, H, G);
+  if (st != OSC_OK) return st;
+  if (S == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
+  if (!X || !QX || !SX) return OSC_E_NULL;
+  if ((L == nullptr) != (B == nullptr)) return OSC_E_NULL;
+  if (!aligned16(X) || !aligned16(QX) || !aligned16(SX) || (B && !aligned16(B))) return OSC_E_ALIGN;
+  osc::TableArg tab;
+  if (L) {
+    st = pack_table(L, H / G, G, &tab);
+    if (st != OSC_OK) return st;
+  }
+  return from_hip(osc::launch_quant(X, S, H, G, L ? &tab : nullptr, L ? osc::kExtractZero : osc::kNoTable, afmt, QX,
+                                    SX, B, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt, void* QW, uint8_t* SW,
+                            void* WL, void* stream) {
+  if (wfmt != OSC_MXFP4 && wfmt != OSC_MXFP8) return OSC_E_FORMAT;
+  osc_status st = check_dims(N, H, G);
+  if (st != OSC_OK) return st;
+  if (N == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
+  if (!W || !QW || !SW) return OSC_E_NULL;
+  if ((L == nullptr) != (WL == nullptr)) return OSC_E_NULL;
+  if (!aligned16(W) || !aligned16(QW) || !aligned16(SW) || (WL && !aligned16(WL))) return OSC_E_ALIGN;
+  osc::TableArg tab;
+  if (L) {
+    st = pack_table(L, H / G, G, &tab);
+    if (st != OSC_OK) return st;
+  }
+  return from_hip(osc::launch_quant(W, N, H, G, L ? &tab : nullptr, L ? osc::kCopyOnly : osc::kNoTable, wfmt, QW, SW,
+                                    WL, static_cast<hipStream_t>(stream)));
+}
+
+static osc_status check_gemm(int S, int N, int H, int G, osc_ytype yt) {
+  if (yt != OSC_Y_BF16 && yt != OSC_Y_F32) return OSC_E_FORMAT;
+  if (S < 0 || N < 0 || H <= 0 || !valid_g(G) || H % 256 != 0) return OSC_E_SHAPE;
+  if (H / G > OSC_MAX_GROUPS) return OSC_E_SHAPE;
+  return OSC_OK;
+}
+
+osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void* QW, const uint8_t* SW,
+                    const void* WL, int S, int N, int H, int G, void* Y, osc_ytype yt, void* stream) {
+  osc_status st = check_gemm(S, N, H, G, yt);
+  if (st != OSC_OK) return st;
+  if ((B == nullptr) != (WL == nullptr)) return OSC_E_NULL;
+  if (B && (H / G) % 8 != 0) return OSC_E_SHAPE;
+  if (S == 0 || N == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
+  if (!QX || !SX || !QW || !SW || !Y) return OSC_E_NULL;
+  if (!aligned16(QX) || !aligned16(SX) || !aligned16(QW) || !aligned16(SW) || !aligned16(Y)) return OSC_E_ALIGN;
+  if (B && (!aligned16(B) || !aligned16(WL))) return OSC_E_ALIGN;
+  osc::GemmArgs a{QX, SX, B, QW, SW, WL, Y, S, N, H, G, OSC_MXFP4, OSC_MXFP4, yt};
+  return from_hip(osc::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, const uint8_t* SW, osc_fmt wfmt, int S,
+                        int N, int H, int G, void* Y, osc_ytype yt, void* stream) {
+  if (wfmt != OSC_MXFP4 && wfmt != OSC_MXFP8) return OSC_E_FORMAT;
+  osc_status st = check_gemm(S, N, H, G, yt);
+  if (st != OSC_OK) return st;
+  if (G == 16) return OSC_E_SHAPE;
+  if (S == 0 || N == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
+  if (!QX8 || !SX || !QW || !SW || !Y) return OSC_E_NULL;
+  if (!aligned16(QX8) || !aligned16(SX) || !aligned16(QW) || !aligned16(SW) || !aligned16(Y)) return OSC_E_ALIGN;
+  osc::GemmArgs a{QX8, SX, nullptr, QW, SW, nullptr, Y, S, N, H, G, OSC_MXFP8, wfmt, yt};
+  return from_hip(osc::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho, int32_t* L,
+                           int32_t* hits, int32_t* events, void* stream) {
+  if (R <= 0) return OSC_E_SHAPE;
+  osc_status st = check_dims(R, H, G);
+  if (st != OSC_OK) return st;
+  if (!(alpha > 0.0) || !(rho > 0.0 && rho <= 1.0)) return OSC_E_SHAPE;
+  if (!Xcal || !L || !hits || !events) return OSC_E_NULL;
+  if (!aligned16(Xcal) || !aligned16(L) || !aligned16(hits) || !aligned16(events)) return OSC_E_ALIGN;
+  return from_hip(osc::launch_build_table(Xcal, R, H, G, alpha, rho, L, hits, events,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Library-internal declarations shared by the HIP translation units of libosc.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "osc.h"
+
+namespace osc {
+
+// Table slice passed by value in the kernel arguments: the per-layer row of the
+// offline table lives in the kernarg segment for the duration of the launch.
+struct TableArg {
+  int8_t v[OSC_MAX_GROUPS];
+};
+
+enum TableMode { kNoTable = 0, kExtractZero = 1, kCopyOnly = 2 };
+
+// Quantize rows of a bf16 matrix in groups of G (activations or weights).
+//   mode kExtractZero: B[r][k] <- X[r][kG+L[k]], that slot is zeroed before scaling.
+//   mode kCopyOnly:    WL[r][k] <- W[r][kG+L[k]], nothing is zeroed.
+hipError_t launch_quant(const void* X, int rows, int H, int G, const TableArg* tab, int mode, osc_fmt fmt,
+                        void* Q, uint8_t* SC, void* side, hipStream_t st);
+
+hipError_t launch_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho, int32_t* L,
+                              int32_t* hits, int32_t* events, hipStream_t st);
+
+struct GemmArgs {
+  const void* QX;
+  const uint8_t* SX;
+  const void* B;
+  const void* QW;
+  const uint8_t* SW;
+  const void* WL;
+  void* Y;
+  int S, N, H, G;
+  osc_fmt afmt, wfmt;
+  osc_ytype yt;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+}  // namespace osc

@@ -1,0 +1,211 @@
+// Group quantization with outlier extraction (OSC page "W4A4量化技术：OSC框架如何实现高效LLM部署",
+// §3.2: copy the table-indexed channel into B, zero it, scale the zeroed group, microscaling-
+// quantize) and the offline weight preparation of §3.3 (same kernel, the indexed channel is
+// copied into the contiguous W_L block without zeroing).
+//
+// Data flow: HBM-bound.  Each lane owns one 16-byte chunk (8 bf16) of a row, so a wavefront
+// reads 1 KiB of consecutive memory and G/8 adjacent lanes form one group.  The group amax is
+// an integer max over the bf16 magnitude bits (|x| ordering == bit ordering for finite values),
+// reduced across the group's lanes with cross-lane swizzles.  The E8M0 code is read straight
+// off the amax exponent field: floor(log2 amax) - emax + 127 = E - 2 (E2M1) or E - 8 (E4M3),
+// floored at 0 (an amax of zero or below 2^-125 gives the minimum scale 2^-127).
+// Element encoding uses gfx950's scaled conversion instructions, which divide by the scale's
+// power of two and round to nearest-even; E2M1 saturates in hardware, E4M3 does not, so
+// E4M3 magnitudes are first clamped to 448 * 2^e (exactly representable in bf16).
+#include "osc_internal.h"
+
+namespace osc {
+namespace {
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short s2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us2, w); }
+__device__ __forceinline__ uint32_t as_u32(us2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
+
+template <int G, int FMT, int MODE>
+__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nchunks, int H, TableArg tab,
+                                               uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
+                                               uint16_t* __restrict__ side) {
+  constexpr int LPG = G / 8;  // lanes per group
+  const long c = (long)blockIdx.x * 256 + threadIdx.x;
+  // nchunks is a multiple of LPG and groups start at multiples of LPG, so a group's lanes
+  // are either all in range or all out of range; the cross-lane reductions stay inside a group.
+  if (c >= nchunks) return;
+  const int cpr = H >> 3;
+  const long r = c / cpr;
+  const int col0 = (int)(c - r * cpr) << 3;
+  const int k = col0 / G;
+  const int q = (col0 % G) >> 3;
+  const int K = H / G;
+
+  const u4 v = __builtin_nontemporal_load(X + c);
+  uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+
+  if (MODE != kNoTable) {
+    const int ent = tab.v[k];
+    const bool own = ent >= 0 && (ent >> 3) == q;
+    uint32_t val = 0;
+    if (own) {
+      const int e = ent & 7;
+      const uint32_t word = (e >> 1) == 0 ? w0 : (e >> 1) == 1 ? w1 : (e >> 1) == 2 ? w2 : w3;
+      val = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+      if (MODE == kExtractZero) {
+        const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        w0 = (e >> 1) == 0 ? (w0 & keep) : w0;
+        w1 = (e >> 1) == 1 ? (w1 & keep) : w1;
+        w2 = (e >> 1) == 2 ? (w2 & keep) : w2;
+        w3 = (e >> 1) == 3 ? (w3 & keep) : w3;
+      }
+    }
+    if (own || (ent < 0 && q == 0)) side[r * K + k] = (uint16_t)val;
+  }
+
+  // group amax over the magnitude bits
+  us2 m = __builtin_elementwise_max(as_us2(w0 & 0x7FFF7FFFu), as_us2(w1 & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, as_us2(w2 & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, as_us2(w3 & 0x7FFF7FFFu));
+  int amax = m.x > m.y ? m.x : m.y;
+#pragma unroll
+  for (int off = 1; off < LPG; off <<= 1) {
+    const int o = __shfl_xor(amax, off, 64);
+    amax = o > amax ? o : amax;
+  }
+  const int E = amax >> 7;
+  const int sx = FMT == OSC_MXFP4 ? (E > 2 ? E - 2 : 0) : (E > 8 ? E - 8 : 0);
+  if (q == 0) SC[r * K + k] = (uint8_t)sx;
+  const float scale = __builtin_bit_cast(float, (uint32_t)sx << 23);  // only the exponent field is used
+
+  if (FMT == OSC_MXFP4) {
+    uint32_t out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w0), scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w1), scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w2), scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w3), scale, 3);
+    __builtin_nontemporal_store(out, reinterpret_cast<uint32_t*>(Q) + c);
+  } else {
+    // saturate: |x| <= 448 * 2^e, i.e. exponent field sx + 8 with mantissa 0b1100000
+    const uint32_t lim = (((uint32_t)sx + 8u) << 7) | 0x60u;
+    const us2 lim2 = {(unsigned short)lim, (unsigned short)lim};
+    w0 = (w0 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w0 & 0x7FFF7FFFu), lim2));
+    w1 = (w1 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w1 & 0x7FFF7FFFu), lim2));
+    w2 = (w2 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w2 & 0x7FFF7FFFu), lim2));
+    w3 = (w3 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w3 & 0x7FFF7FFFu), lim2));
+    s2 o0 = {0, 0}, o1 = {0, 0};
+    o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, as_bf2(w0), scale, false);
+    o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, as_bf2(w1), scale, true);
+    o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, as_bf2(w2), scale, false);
+    o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, as_bf2(w3), scale, true);
+    const u2 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1)};
+    __builtin_nontemporal_store(o, reinterpret_cast<u2*>(Q) + c);
+  }
+}
+
+template <int G, int FMT>
+hipError_t dispatch_mode(const void* X, long nchunks, int H, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+                         void* side, hipStream_t st) {
+  const unsigned grid = (unsigned)((nchunks + 255) / 256);
+  const u4* x = static_cast<const u4*>(X);
+  uint8_t* q = static_cast<uint8_t*>(Q);
+  uint16_t* sd = static_cast<uint16_t*>(side);
+  static const TableArg empty = {};
+  const TableArg& t = tab ? *tab : empty;
+  if (mode == kExtractZero)
+    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, nchunks, H, t, q, SC, sd);
+  else if (mode == kCopyOnly)
+    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, nchunks, H, t, q, SC, sd);
+  else
+    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, nchunks, H, t, q, SC, sd);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t dispatch_fmt(const void* X, long nchunks, int H, const TableArg* tab, int mode, osc_fmt fmt, void* Q,
+                        uint8_t* SC, void* side, hipStream_t st) {
+  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, nchunks, H, tab, mode, Q, SC, side, st);
+  return dispatch_mode<G, OSC_MXFP8>(X, nchunks, H, tab, mode, Q, SC, side, st);
+}
+
+// ------------------------------------------------------------------ table builder
+// §3.1 Algorithm 1 for one (position, layer).  One workgroup per group k; threads stride over
+// calibration rows, each row's event is decided in fp64 (sum of G bf16 magnitudes is exact),
+// and channel histograms are accumulated in LDS.
+template <int G>
+__global__ __launch_bounds__(256) void k_build_table(const uint16_t* __restrict__ X, int R, int H, double alpha,
+                                                     double rho, int32_t* __restrict__ L, int32_t* __restrict__ hits,
+                                                     int32_t* __restrict__ events) {
+  __shared__ int hist[G];
+  __shared__ int nev;
+  const int k = blockIdx.x;
+  for (int j = threadIdx.x; j < G; j += 256) hist[j] = 0;
+  if (threadIdx.x == 0) nev = 0;
+  __syncthreads();
+  int my_events = 0;
+  for (int r = threadIdx.x; r < R; r += 256) {
+    const uint16_t* row = X + (long)r * H + (long)k * G;
+    double sum = 0.0;
+    float m = -1.0f;
+    int jr = 0;
+    for (int j = 0; j < G; ++j) {
+      const float a = fabsf(__builtin_bit_cast(float, (uint32_t)row[j] << 16));
+      sum += (double)a;
+      if (a > m) {
+        m = a;
+        jr = j;
+      }
+    }
+    const double mean = sum / G;
+    if ((double)m > alpha * mean) {
+      atomicAdd(&hist[jr], 1);
+      ++my_events;
+    }
+  }
+  atomicAdd(&nev, my_events);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int js = 0;
+    for (int j = 1; j < G; ++j)
+      if (hist[j] > hist[js]) js = j;
+    const int n = nev;
+    hits[k] = n ? hist[js] : 0;
+    events[k] = n;
+    L[k] = (n > 0 && (double)hist[js] >= rho * (double)R) ? js : -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant(const void* X, int rows, int H, int G, const TableArg* tab, int mode, osc_fmt fmt, void* Q,
+                        uint8_t* SC, void* side, hipStream_t st) {
+  const long nchunks = (long)rows * (H / 8);
+  if (nchunks == 0) return hipSuccess;
+  switch (G) {
+    case 16: return dispatch_fmt<16>(X, nchunks, H, tab, mode, fmt, Q, SC, side, st);
+    case 32: return dispatch_fmt<32>(X, nchunks, H, tab, mode, fmt, Q, SC, side, st);
+    default: return dispatch_fmt<64>(X, nchunks, H, tab, mode, fmt, Q, SC, side, st);
+  }
+}
+
+hipError_t launch_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho, int32_t* L,
+                              int32_t* hits, int32_t* events, hipStream_t st) {
+  const uint16_t* x = static_cast<const uint16_t*>(Xcal);
+  const int K = H / G;
+  switch (G) {
+    case 16:
+      hipLaunchKernelGGL(k_build_table<16>, dim3(K), dim3(256), 0, st, x, R, H, alpha, rho, L, hits, events);
+      break;
+    case 32:
+      hipLaunchKernelGGL(k_build_table<32>, dim3(K), dim3(256), 0, st, x, R, H, alpha, rho, L, hits, events);
+      break;
+    default:
+      hipLaunchKernelGGL(k_build_table<64>, dim3(K), dim3(256), 0, st, x, R, H, alpha, rho, L, hits, events);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace osc
