@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the extra workload rows")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--only", default=None, help="time only this workload row (profiling runs)")
+    p.add_argument("--calib-copy", type=int, default=0, metavar="MB",
+                   help="also run one plain device copy of MB MiB (calibrates HBM traffic counters)")
     return p.parse_args()
 
 
@@ -208,7 +210,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the OSC layer's one-GPU share is the workload; "
-              f"--gpus {args.gpus} is not supported (sharding is described in DESIGN.md, not run)",
+              f"--gpus {args.gpus} is not supported (sharding across GPUs is not part of this measurement)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -220,6 +222,16 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     t_start = time.perf_counter()
+
+    if args.calib_copy:
+        n = args.calib_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- the headline workload: Qwen3-8B QKV projection
     w = synth.qkv(S=2048)

@@ -2,8 +2,7 @@
 
 Argument marshalling only.  Every step runs in the HIP kernels of libosc.so;
 there is no CPU fallback: importing this package fails loudly when the library
-has not been built (``python -m w4a4_outlier_split_amd.build`` or
-``__graft_entry__.build()``).
+has not been built (``python w4a4_outlier_split_amd/build.py``).
 
 Device buffers are torch tensors on a ROCm device (their ``data_ptr()`` is
 passed through); table slices ``L`` are host arrays (numpy int32 or anything
@@ -38,7 +37,7 @@ EXPORTS = ("osc_pack_weights", "osc_quant_act", "osc_gemm", "osc_gemm_fp8", "osc
            "osc_last_device_error")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"libosc.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    raise ImportError(f"libosc.so is not built ({LIB_PATH}); run python w4a4_outlier_split_amd/build.py")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p

@@ -1,27 +1,38 @@
 // Dual-path OSC GEMM on CDNA4 scaled MFMA (OSC page "W4A4量化技术：OSC框架如何实现高效LLM部署",
-// §3.2: Y = (Q_X ⊗ Q_W)·S + B·W_L; §3.3: the 4-bit and 16-bit operand streams are consumed
-// together; §4: FP8 microscaling for the down-projection input).
+// §3.2: Y = (Q_X ⊗ Q_W)·S + B·W_L; §3.3: the 4-bit and the 16-bit operand streams are consumed
+// together by one kernel; §4: FP8 microscaling for the down-projection input).
 //
-// One workgroup = 4 wavefronts computes a BM x BN tile of Y.  Each wavefront owns a
-// (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32x32 blocks; every block's fp32 accumulators
-// (16 per lane) receive both paths:
-//   * the 16-bit compensation B·W_L as v_mfma_f32_32x32x16_bf16 over the K groups (B rows and
-//     W_L rows are K-contiguous, loaded straight into registers while the first main-loop
-//     stage is in flight);
-//   * the main path as v_mfma_scale_f32_32x32x64_f8f6f4: the E8M0 group scales are applied by
-//     the matrix core itself (one scale byte per 32 K-elements per row/column), so there is
-//     no dequantization pass.
-// Both instructions produce the same accumulator layout (lane l holds column l%32, rows
-// 8*(i/4) + 4*(l/32) + i%4 for i < 16), which is what lets the two paths share accumulators.
+// One workgroup of 8 (or 4) wavefronts computes a BM x BN tile of Y; each wavefront owns a
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 blocks whose fp32 accumulators receive both paths:
+//   * the 16-bit compensation B·W_L as v_mfma_f32_32x32x16_bf16 over the K groups;
+//   * the main path as v_mfma_scale_f32_32x32x64_f8f6f4, the E8M0 group scales applied by the
+//     matrix core itself (one scale byte per 32 K-elements per row / column).
+// Both instructions leave the same accumulator layout (lane l holds column l%32, rows
+// 8*(i/4) + 4*(l/32) + i%4 of register i < 16), so the paths share the accumulators.
 //
-// Operand layout of the scaled MFMA (lane l: row l%32 of its operand, half h = l/32):
-//   E2M1: the lane holds the 32 elements [32h, 32h+32) of the 64-deep K slice, 16 bytes,
-//         element 2i in the low nibble of byte i (the canonical packing of the ABI);
-//   E4M3: the lane holds K [16h, 16h+16) in bytes 0..15 and [32+16h, 48+16h) in bytes 16..31.
-//   Scale for 32-block b of row r comes from lane r + 32*b; opsel picks the byte.
-// Main loop: K-steps of BK elements, global -> registers -> LDS (two buffers, one barrier per
-// step); LDS rows are XOR-swizzled in 16-byte chunks so that the 16-byte reads of 8 / 16
-// consecutive rows hit distinct banks.
+// Pipeline.  The K dimension is cut into stages, each one LDS row of 64 bytes per operand row
+// (128 E2M1 codes, or 32 bf16 of B / W_L), 128 bytes for E4M3 rows.  The compensation comes
+// first as ceil(K/32) stages, then H/128 main stages: the same ring, the same fragment reads.
+// Stages are copied global -> LDS by the LDS-DMA path (global_load_lds, 16 bytes per lane,
+// lane order in LDS) into a ring of NS buffers, NS-1 stages ahead of the math, so no VGPRs
+// hold in-flight data and HBM / L2 latency is covered by NS-1 stages of MFMA work.  One
+// barrier per stage; the wait for a stage's DMA is an explicit vmcnt on the loads issued after
+// it.  The E8M0 scale bytes of a stage travel the same way (one dword per lane).
+// A wavefront can keep only a limited number of memory requests in flight, so the rate at which
+// a CU is fed grows with the number of waves issuing loads (measured on MI355X: ~17 B/clk/CU with
+// 4 waves, ~36 with 8).  Hence 8 waves per workgroup, two per SIMD: the first half loads the
+// X-side rows and scales of every stage, the second half the W side.
+// LDS rows are XOR-swizzled in 16-byte chunks: a wavefront's 16-byte fragment reads of 8 or 16
+// consecutive rows then fall on distinct banks.  The swizzle is applied on the global side:
+// lane l of a DMA instruction fills LDS chunk p = 64*q + l, and fetches the logical chunk that
+// belongs there.
+//
+// Operand fragments of the scaled MFMA (lane l: row l%32 of its operand, half h = l/32):
+//   E2M1: K [32h, 32h+32) of the 64-deep slice, 16 bytes, element 2i in the low nibble of byte i;
+//   E4M3: K [16h, 16h+16) in bytes 0..15 and [32+16h, 48+16h) in bytes 16..31;
+//   the scale of 32-block b of row r comes from lane r + 32*b, opsel picks its byte.
+// G=64: both 32-blocks of a group use the same byte.  G=16: each 32-element hardware block holds
+// one 16-group and 16 zero codes (inserted in registers), so every MFMA covers 32 real elements.
 #include "osc_internal.h"
 
 namespace osc {
@@ -29,8 +40,10 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kFp4 = 4;  // scaled-MFMA format codes
 constexpr int kFp8 = 0;
@@ -38,88 +51,109 @@ constexpr int kFp8 = 0;
 __device__ __forceinline__ v8i widen(v4i lo) { return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1); }
 __device__ __forceinline__ v8i join(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
 
-// swizzled 16-byte chunk position of logical chunk cc in row r, for rows of RB bytes
+// swizzled position of logical 16-byte chunk cc in LDS row r, for rows of RB bytes
 template <int RB>
 __device__ __forceinline__ int swz(int r, int cc) {
   if constexpr (RB == 64) return cc ^ (((r >> 1) ^ (r >> 3)) & 3);
-  else if constexpr (RB == 128) return cc ^ ((r ^ (r >> 3)) & 7);
-  else return cc ^ (r & 15);
+  else return cc ^ ((r ^ (r >> 3)) & 7);
 }
 
-template <int FA, int FB, int G, bool COMP, int YT, int BM, int BN, int WAVES_M>
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int kEnc = (N & 15) | ((N >> 4) << 14) | 0xF70;
+  __builtin_amdgcn_s_waitcnt(kEnc);
+}
+
+// Workgroup barrier that orders LDS only: no vmcnt wait (the DMA ring keeps loads in flight
+// across it); the memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void dma16(const void* g, lds_u8* __restrict__ l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, lds_u8* __restrict__ l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
+template <int FA, int FB, int G, bool COMP, int BM, int BN, int WAVES_M, int WAVES_N, int NS>
 struct Cfg {
-  static constexpr int WAVES_N = 4 / WAVES_M;
-  static constexpr int WTM = BM / WAVES_M;  // wave tile rows
+  static constexpr int NW = WAVES_M * WAVES_N;     // wavefronts per workgroup
+  static constexpr int NCW = NW / 2;               // wavefronts per DMA class (X side / W side)
+  static constexpr int WTM = BM / WAVES_M;
   static constexpr int WTN = BN / WAVES_N;
   static constexpr int TM = WTM / 32;
   static constexpr int TN = WTN / 32;
-  static constexpr int BK = (FA == kFp4 && FB == kFp4) ? 256 : 128;  // K elements per stage
-  static constexpr int RBA = FA == kFp4 ? BK / 2 : BK;                 // LDS row bytes
-  static constexpr int RBB = FB == kFp4 ? BK / 2 : BK;
-  static constexpr int STAGE = BM * RBA + BN * RBB;
-  static constexpr int CHA = BM * RBA / 16 / 256;  // 16-byte chunks per thread per stage
-  static constexpr int CHB = BN * RBB / 16 / 256;
-  static constexpr int MFMA_K = (G == 16) ? 32 : 64;  // real K elements per scaled MFMA
-  static constexpr int NMF = BK / MFMA_K;              // scaled MFMAs per stage per block
-  static constexpr int SB = BK / G;                    // scale bytes per row per stage
-  static_assert(TM >= 1 && TN >= 1 && CHA >= 1 && CHB >= 1, "tile too small");
-  static_assert(BM * RBA % (16 * 256) == 0 && BN * RBB % (16 * 256) == 0, "tile / thread mismatch");
+  static constexpr int BK = 128;  // K elements per main stage
+  static constexpr int RBA = FA == kFp4 ? 64 : 128;
+  static constexpr int RBB = FB == kFp4 ? 64 : 128;
+  static constexpr int RPI_A = 1024 / RBA;  // rows per DMA wave-instruction
+  static constexpr int RPI_B = 1024 / RBB;
+  static constexpr int AROWS = (BM + NCW * RPI_A - 1) / (NCW * RPI_A) * (NCW * RPI_A);
+  static constexpr int BROWS = (BN + NCW * RPI_B - 1) / (NCW * RPI_B) * (NCW * RPI_B);
+  static constexpr int NIA = AROWS / RPI_A / NCW;  // row DMA instructions per X-side wave per stage
+  static constexpr int NIB = BROWS / RPI_B / NCW;
+  static constexpr int NIMAX = NIA > NIB ? NIA : NIB;
+  static constexpr int SB = BK / G;                // scale bytes per row per stage: 8, 4 or 2
+  // Scales travel as whole dwords (LDS DMA packs 4 bytes per lane); with G=64 a stage's two
+  // bytes are half of the aligned dword shared with the neighbouring stage.
+  static constexpr int SBL = SB >= 4 ? SB : 4;     // LDS scale bytes per row per stage
+  static constexpr int SLPR = SBL / 4;             // lanes per scale row
+  static constexpr int SRPI = 64 / SLPR;           // scale rows per DMA wave-instruction
+  static constexpr int SROWS_A = (BM + NCW * SRPI - 1) / (NCW * SRPI) * (NCW * SRPI);
+  static constexpr int SROWS_B = (BN + NCW * SRPI - 1) / (NCW * SRPI) * (NCW * SRPI);
+  static constexpr int SCA = SROWS_A / SRPI / NCW; // scale DMA instructions per X-side wave
+  static constexpr int SCB = SROWS_B / SRPI / NCW;
+  static constexpr int SCMAX = SCA > SCB ? SCA : SCB;
+  static constexpr int DA = NIA + SCA;             // DMA instructions per wave per stage
+  static constexpr int DB = NIB + SCB;
+  static constexpr int OFF_B = AROWS * RBA;
+  static constexpr int OFF_SA = OFF_B + BROWS * RBB;
+  static constexpr int OFF_SB = OFF_SA + SROWS_A * SBL;
+  static constexpr int STAGE = OFF_SB + SROWS_B * SBL;
+  static constexpr int NMF = (G == 16) ? 4 : 2;    // scaled MFMAs per stage per block
+  static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(!COMP || FA == kFp4, "compensation stages reuse the 64-byte E2M1 row geometry");
 };
 
-// scale bytes of one row for one stage, as up to four dwords
-template <int SB>
-__device__ __forceinline__ void load_scales(const uint8_t* p, uint32_t (&s)[4]) {
-  if constexpr (SB == 16) {
-    v4i v = *reinterpret_cast<const v4i*>(p);
-    s[0] = v[0]; s[1] = v[1]; s[2] = v[2]; s[3] = v[3];
-  } else if constexpr (SB == 8) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
-    s[0] = v.x; s[1] = v.y; s[2] = 0; s[3] = 0;
-  } else if constexpr (SB == 4) {
-    s[0] = *reinterpret_cast<const uint32_t*>(p); s[1] = s[2] = s[3] = 0;
-  } else {
-    s[0] = *reinterpret_cast<const uint16_t*>(p); s[1] = s[2] = s[3] = 0;
-  }
+template <int FA, int FB, int G, int BM, int BN, int WAVES_M, int WAVES_N>
+constexpr int ring_depth() {
+  constexpr int n = (160 * 1024) / Cfg<FA, FB, G, false, BM, BN, WAVES_M, WAVES_N, 2>::STAGE;
+  return n > 4 ? 4 : n;
 }
 
-// Scale register and opsel for scaled MFMA number m of a stage, for a lane of half h.
-// G=32: 32-block b = 2m + h lives in byte b of the row's stage scales.
-// G=64: both halves use group m (byte m).  G=16: MFMA m covers groups 2m, 2m+1, lane h
-// holds group 2m + h (padded with zeros), so it needs byte 2m + h.
-template <int G, int FMTA>
-__device__ __forceinline__ uint32_t scale_reg(const uint32_t (&s)[4], int m, int h) {
-  if constexpr (G == 64) {
-    return s[m >> 2];
-  } else {
-    const int b = 2 * m + h;
-    return s[b >> 2] >> (8 * (b & 3));
-  }
+template <int N, int D>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  // ahead = number of later stages whose DMA is already issued (0 .. N)
+  if constexpr (N >= 3) { if (ahead >= 3) { wait_vm<3 * D>(); return; } }
+  if constexpr (N >= 2) { if (ahead == 2) { wait_vm<2 * D>(); return; } }
+  if constexpr (N >= 1) { if (ahead == 1) { wait_vm<D>(); return; } }
+  wait_vm<0>();
 }
 
-template <int G>
-__device__ __forceinline__ constexpr int scale_opsel(int m) {
-  return G == 64 ? (m & 3) : 0;
-}
-
-template <int FA, int FB, int G, bool COMP, int YT, int BM, int BN, int WAVES_M>
-__global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX,
-                                                 const uint16_t* __restrict__ Bc, const uint8_t* __restrict__ QW,
-                                                 const uint8_t* __restrict__ SW, const uint16_t* __restrict__ WL,
-                                                 void* __restrict__ Y, int S, int N, int H) {
-  using C = Cfg<FA, FB, G, COMP, YT, BM, BN, WAVES_M>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+template <int FA, int FB, int G, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N, int NS>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
+    const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX, const uint8_t* __restrict__ Bc,
+    const uint8_t* __restrict__ QW, const uint8_t* __restrict__ SW, const uint8_t* __restrict__ WL,
+    void* __restrict__ Y, int S, int N, int H) {
+  using C = Cfg<FA, FB, G, COMP, BM, BN, WAVES_M, WAVES_N, NS>;
+  static_assert(NS >= 3 && NS * C::STAGE <= 160 * 1024, "the LDS ring must hold at least 3 stages");
+  static_assert(C::DA * (NS - 2) < 64 && C::DB * (NS - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * C::STAGE];
+  lds_u8* const smem = (lds_u8*)smem_raw;
 
   const int K = H / G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / C::WAVES_N;
-  const int wn = wave % C::WAVES_N;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
   const int lr = lane & 31;
   const int h = lane >> 5;
 
-  // tile index, XCD-aware: workgroups go round-robin over the 8 XCDs, so give each XCD a
-  // contiguous run of tiles (M fastest) that share W column panels in its L2.
+  // XCD-aware tile order: workgroups go round-robin over the 8 XCDs; give each XCD a contiguous
+  // run of tiles (M fastest) so that the tiles sharing a W panel share that XCD's L2.
   const int ntm = (S + BM - 1) / BM;
   const int ntn = (N + BN - 1) / BN;
   const int total = ntm * ntn;
@@ -130,6 +164,76 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ QX,
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
+  const int nks = H / C::BK;
+  const int ncs = COMP ? (K + 31) / 32 : 0;  // compensation stages (32 groups each)
+  const int nst = ncs + nks;
+
+  // ------------------------------------------------------------ per-lane DMA sources
+  // X-side waves (wave < NCW) load the QX (or B) rows and the SX scales; W-side waves the QW
+  // (or W_L) rows and SW scales.  Row wave-instruction q = NCW*i + cw fills LDS chunks
+  // [64q, 64q+64) of its region; lane l -> chunk p = 64q + l.
+  const bool xside = wave < C::NCW;
+  const int cw = xside ? wave : wave - C::NCW;
+  const int rb_g = xside ? (FA == kFp4 ? H / 2 : H) : (FB == kFp4 ? H / 2 : H);   // global row bytes
+  const int rb_l = xside ? C::RBA : C::RBB;                                        // LDS row bytes
+  const int r0 = xside ? m0 : n0;
+  const int rmax = (xside ? S : N) - 1;
+  const uint8_t* const gcodes = xside ? QX : QW;
+  const uint8_t* const gcomp = xside ? Bc : WL;
+  const uint8_t* const gscale = xside ? SX : SW;
+  const int ni = xside ? C::NIA : C::NIB;
+  const int nsc = xside ? C::SCA : C::SCB;
+  const int dst_rows = xside ? 0 : C::OFF_B;
+  const int dst_scale = xside ? C::OFF_SA : C::OFF_SB;
+  const uint8_t* src[C::NIMAX];
+  const uint8_t* srcC[COMP ? C::NIMAX : 1];
+  int ccv[C::NIMAX];
+#pragma unroll
+  for (int i = 0; i < C::NIMAX; ++i) {
+    const int p = (C::NCW * i + cw) * 64 + lane;
+    const int cpr = rb_l / 16;
+    const int r = p / cpr;
+    const int pc = p % cpr;
+    const int cc = rb_l == 64 ? swz<64>(r, pc) : swz<128>(r, pc);
+    const long gr = min(r0 + r, rmax);  // ragged edge: clamped rows are never stored
+    src[i] = gcodes + gr * rb_g + cc * 16;
+    ccv[i] = cc;
+    if constexpr (COMP) srcC[i] = gcomp + gr * (2L * K);
+  }
+  // scale bytes: lane l of wave-instruction q covers row q*SRPI + l/SLPR, bytes 4*(l%SLPR)
+  const uint8_t* srcS[C::SCMAX];
+#pragma unroll
+  for (int i = 0; i < C::SCMAX; ++i) {
+    const int q = C::NCW * i + cw;
+    const int r = q * C::SRPI + lane / C::SLPR;
+    srcS[i] = gscale + (long)min(r0 + r, rmax) * K + (lane % C::SLPR) * 4;
+  }
+
+  auto issue = [&](int st, lds_u8* __restrict__ buf) {
+    const bool comp = COMP && st < ncs;
+    if (comp) {
+#pragma unroll
+      for (int i = 0; i < C::NIMAX; ++i) {
+        if (i < ni) {
+          const bool ok = 32 * st + 8 * ccv[i] < K;  // chunks past K: any valid address, zeroed at use
+          dma16(srcC[COMP ? i : 0] + (ok ? 64 * st + 16 * ccv[i] : 0), buf + dst_rows + (C::NCW * i + cw) * 1024);
+        }
+      }
+    } else {
+      const long off = (long)(st - ncs) * rb_l;
+#pragma unroll
+      for (int i = 0; i < C::NIMAX; ++i)
+        if (i < ni) dma16(src[i] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
+    }
+    // scales (also issued for compensation stages, from stage 0, so every stage has the same
+    // number of loads per wave)
+    const int ks = comp ? 0 : st - ncs;
+    const int soff = C::SB >= 4 ? ks * C::SB : (ks >> 1) * 4;
+#pragma unroll
+    for (int i = 0; i < C::SCMAX; ++i)
+      if (i < nsc) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);
+  };
+
   v16f acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -138,225 +242,253 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const uint8_t* __restrict__ QX,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // ---------------------------------------------------------------- global -> LDS staging
-  const long rowbytes_a = FA == kFp4 ? H / 2 : H;
-  const long rowbytes_b = FB == kFp4 ? H / 2 : H;
-  constexpr int CPRA = C::RBA / 16;  // chunks per LDS row
-  constexpr int CPRB = C::RBB / 16;
-  const uint8_t* ga[C::CHA];
-  const uint8_t* gb[C::CHB];
-  int la[C::CHA], lb[C::CHB];
+  // prologue: NS-1 stages in flight
 #pragma unroll
-  for (int i = 0; i < C::CHA; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / CPRA, cc = c % CPRA;
-    const int gr = min(m0 + r, S - 1);  // ragged edge: clamp, results for these rows are not stored
-    ga[i] = QX + (long)gr * rowbytes_a + cc * 16;
-    la[i] = r * C::RBA + swz<C::RBA>(r, cc) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < C::CHB; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / CPRB, cc = c % CPRB;
-    const int gr = min(n0 + r, N - 1);
-    gb[i] = QW + (long)gr * rowbytes_b + cc * 16;
-    lb[i] = BM * C::RBA + r * C::RBB + swz<C::RBB>(r, cc) * 16;
-  }
-  v4i ra[C::CHA], rb[C::CHB];
-  auto gload = [&](int ks) {
-    const long offa = (long)ks * C::RBA, offb = (long)ks * C::RBB;
-#pragma unroll
-    for (int i = 0; i < C::CHA; ++i) ra[i] = *reinterpret_cast<const v4i*>(ga[i] + offa);
-#pragma unroll
-    for (int i = 0; i < C::CHB; ++i) rb[i] = *reinterpret_cast<const v4i*>(gb[i] + offb);
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* base = smem + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::CHA; ++i) *reinterpret_cast<v4i*>(base + la[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < C::CHB; ++i) *reinterpret_cast<v4i*>(base + lb[i]) = rb[i];
-  };
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nst) issue(s, smem + s * C::STAGE);
 
-  // scale rows owned by this lane
-  const uint8_t* psa[C::TM];
-  const uint8_t* psb[C::TN];
+  int arow[C::TM], brow[C::TN];
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) psa[i] = SX + (long)min(m0 + wm * C::WTM + 32 * i + lr, S - 1) * K;
+  for (int i = 0; i < C::TM; ++i) arow[i] = wm * C::WTM + 32 * i + lr;
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j) psb[j] = SW + (long)min(n0 + wn * C::WTN + 32 * j + lr, N - 1) * K;
-  uint32_t sa[C::TM][4], sb[C::TN][4], sa_n[C::TM][4], sb_n[C::TN][4];
-  auto sload = [&](int ks, uint32_t (&xa)[C::TM][4], uint32_t (&xb)[C::TN][4]) {
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) load_scales<C::SB>(psa[i] + ks * C::SB, xa[i]);
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) load_scales<C::SB>(psb[j] + ks * C::SB, xb[j]);
+  for (int j = 0; j < C::TN; ++j) brow[j] = wn * C::WTN + 32 * j + lr;
+
+  // ------------------------------------------------------------ fragments and scales
+  // A stage is consumed in two halves.  Compensation stages: half hf = 16 groups
+  // (v_mfma_f32_32x32x16_bf16).  Main stages: half hf = NSH scaled MFMAs (NSH = 1, or 2 for G=16).
+  constexpr int NSH = C::NMF / 2;
+  struct Frag {
+    v4i alo[NSH][C::TM], ahi[NSH][C::TM];
+    v4i blo[NSH][C::TN], bhi[NSH][C::TN];
   };
+  struct Scales {
+    uint32_t a[C::TM][2], b[C::TN][2];
+  };
+  auto lds4 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v4i*)p; };
+  auto lds2 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v2i*)p; };
 
-  const int nks = H / C::BK;
-  gload(0);
-  sload(0, sa, sb);
-
-  // ---------------------------------------------------------------- 16-bit compensation path
-  if constexpr (COMP) {
-    const uint16_t* pb[C::TM];
-    const uint16_t* pw[C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) pb[i] = Bc + (long)min(m0 + wm * C::WTM + 32 * i + lr, S - 1) * K + 8 * h;
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) pw[j] = WL + (long)min(n0 + wn * C::WTN + 32 * j + lr, N - 1) * K + 8 * h;
-    const int ncs = (K + 15) / 16;
-    for (int cs = 0; cs < ncs; ++cs) {
-      const bool valid = 16 * cs + 8 * h < K;  // K % 8 == 0: an 8-element chunk is all in or all out
-      v8bf a[C::TM], b[C::TN];
+  auto read_half = [&](int st, int hf, Frag& f) {
+    const lds_u8* __restrict__ As = smem + (st % NS) * C::STAGE;
+    const lds_u8* __restrict__ Bs = As + C::OFF_B;
+    if (COMP && st < ncs) {
+      const bool valid = 32 * st + 16 * hf + 8 * h < K;  // chunks past K are zero operands
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        v4i t = valid ? *reinterpret_cast<const v4i*>(pb[i] + 16 * cs) : v4i{0, 0, 0, 0};
-        a[i] = __builtin_bit_cast(v8bf, t);
+        const v4i t = lds4(As + arow[i] * 64 + swz<64>(arow[i], 2 * hf + h) * 16);
+        f.alo[0][i] = valid ? t : v4i{0, 0, 0, 0};
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        v4i t = valid ? *reinterpret_cast<const v4i*>(pw[j] + 16 * cs) : v4i{0, 0, 0, 0};
-        b[j] = __builtin_bit_cast(v8bf, t);
+        const v4i t = lds4(Bs + brow[j] * 64 + swz<64>(brow[j], 2 * hf + h) * 16);
+        f.blo[0][j] = valid ? t : v4i{0, 0, 0, 0};
       }
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      return;
     }
-  }
-
-  lstore(0);
-  __syncthreads();
-
-  // ---------------------------------------------------------------- 4-bit / 8-bit main path
-  const int arow0 = wm * C::WTM + lr;
-  const int brow0 = wn * C::WTN + lr;
-  for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nks;
-    if (more) {
-      gload(ks + 1);
-      sload(ks + 1, sa_n, sb_n);
-    }
-    const uint8_t* As = smem + cur * C::STAGE;
-    const uint8_t* Bs = As + BM * C::RBA;
 #pragma unroll
-    for (int m = 0; m < C::NMF; ++m) {
-      v8i a[C::TM], b[C::TN];
+    for (int sm = 0; sm < NSH; ++sm) {
+      const int m = hf * NSH + sm;
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        const int r = arow0 + 32 * i;
+        const int r = arow[i];
         if constexpr (FA == kFp4) {
           if constexpr (G == 16) {
-            // 16 real elements: bytes [8(2m+h), +8) of the stage row, zero padded
-            const int byte = 8 * (2 * m + h);
-            const uint2 d = *reinterpret_cast<const uint2*>(As + r * C::RBA + swz<C::RBA>(r, byte >> 4) * 16 + (byte & 15));
-            a[i] = widen(v4i{(int)d.x, (int)d.y, 0, 0});
+            const v2i d = lds2(As + r * 64 + swz<64>(r, m) * 16 + 8 * h);
+            f.alo[sm][i] = v4i{d[0], d[1], 0, 0};
           } else {
-            const int cc = 2 * m + h;
-            a[i] = widen(*reinterpret_cast<const v4i*>(As + r * C::RBA + swz<C::RBA>(r, cc) * 16));
+            f.alo[sm][i] = lds4(As + r * 64 + swz<64>(r, 2 * m + h) * 16);
           }
         } else {
-          const v4i lo = *reinterpret_cast<const v4i*>(As + r * C::RBA + swz<C::RBA>(r, 4 * m + h) * 16);
-          const v4i hi = *reinterpret_cast<const v4i*>(As + r * C::RBA + swz<C::RBA>(r, 4 * m + 2 + h) * 16);
-          a[i] = join(lo, hi);
+          f.alo[sm][i] = lds4(As + r * 128 + swz<128>(r, 4 * m + h) * 16);
+          f.ahi[sm][i] = lds4(As + r * 128 + swz<128>(r, 4 * m + 2 + h) * 16);
         }
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        const int r = brow0 + 32 * j;
+        const int r = brow[j];
         if constexpr (FB == kFp4) {
           if constexpr (G == 16) {
-            const int byte = 8 * (2 * m + h);
-            const uint2 d = *reinterpret_cast<const uint2*>(Bs + r * C::RBB + swz<C::RBB>(r, byte >> 4) * 16 + (byte & 15));
-            b[j] = widen(v4i{(int)d.x, (int)d.y, 0, 0});
+            const v2i d = lds2(Bs + r * 64 + swz<64>(r, m) * 16 + 8 * h);
+            f.blo[sm][j] = v4i{d[0], d[1], 0, 0};
           } else {
-            const int cc = 2 * m + h;
-            b[j] = widen(*reinterpret_cast<const v4i*>(Bs + r * C::RBB + swz<C::RBB>(r, cc) * 16));
+            f.blo[sm][j] = lds4(Bs + r * 64 + swz<64>(r, 2 * m + h) * 16);
           }
         } else {
-          const v4i lo = *reinterpret_cast<const v4i*>(Bs + r * C::RBB + swz<C::RBB>(r, 4 * m + h) * 16);
-          const v4i hi = *reinterpret_cast<const v4i*>(Bs + r * C::RBB + swz<C::RBB>(r, 4 * m + 2 + h) * 16);
-          b[j] = join(lo, hi);
+          f.blo[sm][j] = lds4(Bs + r * 128 + swz<128>(r, 4 * m + h) * 16);
+          f.bhi[sm][j] = lds4(Bs + r * 128 + swz<128>(r, 4 * m + 2 + h) * 16);
         }
       }
-      constexpr int OPS = scale_opsel<G>(0);
-      (void)OPS;
+    }
+  };
+
+  auto read_scales = [&](int st, Scales& sc) {
+    const lds_u8* __restrict__ SAs = smem + (st % NS) * C::STAGE + C::OFF_SA;
+    const lds_u8* __restrict__ SBs = smem + (st % NS) * C::STAGE + C::OFF_SB;
+    const int hsh = (C::SB >= 4) ? 0 : 16 * ((st - ncs) & 1);  // G=64: this stage's half of the dword
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const lds_u8* p = SAs + arow[i] * C::SBL;
+      if constexpr (C::SBL == 8) {
+        const v2i v = lds2(p);
+        sc.a[i][0] = v[0]; sc.a[i][1] = v[1];
+      } else {
+        sc.a[i][0] = *(const __attribute__((address_space(3))) uint32_t*)p >> hsh; sc.a[i][1] = 0;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const lds_u8* p = SBs + brow[j] * C::SBL;
+      if constexpr (C::SBL == 8) {
+        const v2i v = lds2(p);
+        sc.b[j][0] = v[0]; sc.b[j][1] = v[1];
+      } else {
+        sc.b[j][0] = *(const __attribute__((address_space(3))) uint32_t*)p >> hsh; sc.b[j][1] = 0;
+      }
+    }
+  };
+
+  auto mfma_comp = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, f.alo[0][i]),
+                                                            __builtin_bit_cast(v8bf, f.blo[0][j]), acc[i][j], 0, 0, 0);
+  };
+
+  auto mfma_main = [&](int hf, const Frag& f, const Scales& sc) {
+#pragma unroll
+    for (int sm = 0; sm < NSH; ++sm) {
+      const int m = hf * NSH + sm;
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        const uint32_t xs = scale_reg<G, FA>(sa[i], m, h);
+        const v8i a = FA == kFp4 ? widen(f.alo[sm][i]) : join(f.alo[sm][i], f.ahi[sm][i]);
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-          const uint32_t ws = scale_reg<G, FB>(sb[j], m, h);
+          const v8i b = FB == kFp4 ? widen(f.blo[sm][j]) : join(f.blo[sm][j], f.bhi[sm][j]);
           if constexpr (G == 64) {
-            // opsel must be an immediate: the group byte is m & 3 of dword m >> 2
-            switch (m & 3) {
-              case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 0, xs, 0, ws); break;
-              case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 1, xs, 1, ws); break;
-              case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 2, xs, 2, ws); break;
-              default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 3, xs, 3, ws); break;
-            }
+            // group m of the stage: byte m of both operands' scale words, for both halves
+            if (m == 0)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], FA, FB, 0, sc.a[i][0], 0, sc.b[j][0]);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], FA, FB, 1, sc.a[i][0], 1, sc.b[j][0]);
           } else {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 0, xs, 0, ws);
+            // 32-block (G=32) or 16-group (G=16) index 2m + h of the stage's scale bytes
+            const int bidx = 2 * m + h;
+            const uint32_t xs = sc.a[i][bidx >> 2] >> (8 * (bidx & 3));
+            const uint32_t ws = sc.b[j][bidx >> 2] >> (8 * (bidx & 3));
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], FA, FB, 0, xs, 0, ws);
           }
         }
       }
     }
-    if (more) {
-      lstore(cur ^ 1);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sa[i][q] = sa_n[i][q];
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sb[j][q] = sb_n[j][q];
+  };
+
+  // Middle of stage st: wait for this wave's DMA of stage st+1, barrier (stage st+1 visible to
+  // all; stage st-1 no longer read by anyone), refill the freed buffer with stage st+NS-1.
+  auto middle = [&](int st) {
+    if (st + 1 < nst) {
+      const int pending = min(NS - 3, nst - 2 - st);  // stages issued after st+1
+      if (xside) wait_stage<NS - 3, C::DA>(pending);
+      else wait_stage<NS - 3, C::DB>(pending);
     }
-    __syncthreads();
+    lds_barrier();
+    if (st + NS - 1 < nst) issue(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE);
+  };
+
+  // Pipeline: the second half's operands are read before the first half's MFMAs, the next
+  // stage's first-half operands right after the mid-stage barrier, so that every MFMA finds its
+  // operands in registers and the barrier is the only bubble.  Two loops over the one ring keep
+  // one kind of MFMA per loop body.
+  Frag f0, f1;
+  Scales sc, scn;
+  {
+    const int pending = min(NS - 2, nst - 1);  // stages issued after stage 0
+    if (xside) wait_stage<NS - 2, C::DA>(pending);
+    else wait_stage<NS - 2, C::DB>(pending);
+  }
+  lds_barrier();
+  read_half(0, 0, f0);
+  if (!(COMP && 0 < ncs)) read_scales(0, sc);
+
+  int st = 0;
+  if constexpr (COMP) {
+    for (; st < ncs; ++st) {
+      read_half(st, 1, f1);
+      mfma_comp(f0);
+      middle(st);
+      if (st + 1 < nst) {
+        read_half(st + 1, 0, f0);
+        if (st + 1 >= ncs) read_scales(st + 1, scn);
+      }
+      mfma_comp(f1);
+      sc = scn;
+    }
+  }
+  for (; st < nst; ++st) {
+    read_half(st, 1, f1);
+    mfma_main(0, f0, sc);
+    middle(st);
+    if (st + 1 < nst) {
+      read_half(st + 1, 0, f0);
+      read_scales(st + 1, scn);
+    }
+    mfma_main(1, f1, sc);
+    sc = scn;
   }
 
   // ---------------------------------------------------------------- epilogue
+  auto store = [&](bool guard) {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
+    for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int col = n0 + wn * C::WTN + 32 * j + lr;
-      if (col >= N) continue;
+      for (int j = 0; j < C::TN; ++j) {
+        const int col = n0 + wn * C::WTN + 32 * j + lr;
+        const int rbase = m0 + wm * C::WTM + 32 * i + 4 * h;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * C::WTM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < S) {
-          if constexpr (YT == OSC_Y_F32)
-            static_cast<float*>(Y)[(long)row * N + col] = acc[i][j][r];
-          else
-            static_cast<__bf16*>(Y)[(long)row * N + col] = (__bf16)acc[i][j][r];
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + 8 * (r >> 2) + (r & 3);
+          if (!guard || (row < S && col < N)) {
+            if constexpr (YT == OSC_Y_F32)
+              static_cast<float*>(Y)[(long)row * N + col] = acc[i][j][r];
+            else
+              static_cast<__bf16*>(Y)[(long)row * N + col] = (__bf16)acc[i][j][r];
+          }
         }
       }
     }
-  }
+  };
+  if (m0 + BM <= S && n0 + BN <= N)
+    store(false);  // whole tile in range: no per-element guards
+  else
+    store(true);
 }
 
-template <int FA, int FB, int G, bool COMP, int YT, int BM, int BN, int WAVES_M>
+template <int FA, int FB, int G, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
+  constexpr int NS = ring_depth<FA, FB, G, BM, BN, WAVES_M, WAVES_N>();
   const int tiles = ((a.S + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm<FA, FB, G, COMP, YT, BM, BN, WAVES_M>), dim3(tiles), dim3(256), 0, st,
-                     static_cast<const uint8_t*>(a.QX), a.SX, static_cast<const uint16_t*>(a.B),
-                     static_cast<const uint8_t*>(a.QW), a.SW, static_cast<const uint16_t*>(a.WL), a.Y, a.S, a.N, a.H);
+  hipLaunchKernelGGL((k_gemm<FA, FB, G, COMP, YT, BM, BN, WAVES_M, WAVES_N, NS>), dim3(tiles),
+                     dim3(WAVES_M * WAVES_N * 64), 0, st, static_cast<const uint8_t*>(a.QX), a.SX,
+                     static_cast<const uint8_t*>(a.B), static_cast<const uint8_t*>(a.QW), a.SW,
+                     static_cast<const uint8_t*>(a.WL), a.Y, a.S, a.N, a.H);
   return hipGetLastError();
 }
 
 // Tile choice per shape (the MI355X reading of the page's "adaptive resource scheduling",
-// §3.3): big tiles when there are enough of them to cover the 256 CUs, smaller otherwise.
+// §3.3): the largest tile that still yields enough tiles to cover the 256 CUs.  256x256 and
+// 256x192 only where their wavefront sub-tiles fit the register file without spilling (E2M1
+// operands with G = 32 or 64); G = 16 and E4M3 activations use 256x128.
 template <int FA, int FB, int G, bool COMP, int YT>
 hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
   auto tiles = [&](int bm, int bn) { return (long)((a.S + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  if (tiles(256, 256) >= 512) return run<FA, FB, G, COMP, YT, 256, 256, 2>(a, st);
-  if (a.N % 192 == 0 && tiles(256, 192) >= 200) return run<FA, FB, G, COMP, YT, 256, 192, 2>(a, st);
-  if (tiles(128, 128) >= 200) return run<FA, FB, G, COMP, YT, 128, 128, 2>(a, st);
-  return run<FA, FB, G, COMP, YT, 64, 64, 2>(a, st);
+  constexpr bool big = FA == kFp4 && FB == kFp4 && G != 16;
+  if constexpr (big) {
+    if (tiles(256, 256) >= 512) return run<FA, FB, G, COMP, YT, 256, 256, 4, 2>(a, st);
+    if (a.N % 192 == 0 && tiles(256, 192) >= 200) return run<FA, FB, G, COMP, YT, 256, 192, 4, 2>(a, st);
+  }
+  if (tiles(256, 128) >= 200) return run<FA, FB, G, COMP, YT, 256, 128, 4, 2>(a, st);
+  if (tiles(128, 128) >= 200) return run<FA, FB, G, COMP, YT, 128, 128, 4, 2>(a, st);
+  return run<FA, FB, G, COMP, YT, 64, 64, 2, 2>(a, st);
 }
 
 template <int FA, int FB, int G>
@@ -365,6 +497,12 @@ hipError_t pick_comp(const GemmArgs& a, hipStream_t st) {
   if (a.yt == OSC_Y_F32)
     return comp ? pick_tile<FA, FB, G, true, OSC_Y_F32>(a, st) : pick_tile<FA, FB, G, false, OSC_Y_F32>(a, st);
   return comp ? pick_tile<FA, FB, G, true, OSC_Y_BF16>(a, st) : pick_tile<FA, FB, G, false, OSC_Y_BF16>(a, st);
+}
+
+template <int FA, int FB, int G>
+hipError_t pick_nocomp(const GemmArgs& a, hipStream_t st) {
+  if (a.yt == OSC_Y_F32) return pick_tile<FA, FB, G, false, OSC_Y_F32>(a, st);
+  return pick_tile<FA, FB, G, false, OSC_Y_BF16>(a, st);
 }
 
 }  // namespace
@@ -378,16 +516,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       default: return pick_comp<kFp4, kFp4, 64>(a, st);
     }
   }
-  // FP8 activations, no compensation path
-  GemmArgs b = a;
-  b.B = nullptr;
-  b.WL = nullptr;
+  // FP8 activations: no compensation path
   if (a.wfmt == OSC_MXFP4) {
-    if (a.G == 32) return pick_comp<kFp8, kFp4, 32>(b, st);
-    return pick_comp<kFp8, kFp4, 64>(b, st);
+    if (a.G == 32) return pick_nocomp<kFp8, kFp4, 32>(a, st);
+    return pick_nocomp<kFp8, kFp4, 64>(a, st);
   }
-  if (a.G == 32) return pick_comp<kFp8, kFp8, 32>(b, st);
-  return pick_comp<kFp8, kFp8, 64>(b, st);
+  if (a.G == 32) return pick_nocomp<kFp8, kFp8, 32>(a, st);
+  return pick_nocomp<kFp8, kFp8, 64>(a, st);
 }
 
 }  // namespace osc
