@@ -123,15 +123,6 @@ constexpr int ring_depth() {
   return n > 4 ? 4 : n;
 }
 
-template <int N, int D>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  // ahead = number of later stages whose DMA is already issued (0 .. N)
-  if constexpr (N >= 3) { if (ahead >= 3) { wait_vm<3 * D>(); return; } }
-  if constexpr (N >= 2) { if (ahead == 2) { wait_vm<2 * D>(); return; } }
-  if constexpr (N >= 1) { if (ahead == 1) { wait_vm<D>(); return; } }
-  wait_vm<0>();
-}
-
 template <int FA, int FB, int G, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N, int NS>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX, const uint8_t* __restrict__ Bc,
@@ -209,8 +200,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     srcS[i] = gscale + (long)min(r0 + r, rmax) * K + (lane % C::SLPR) * 4;
   }
 
-  auto issue = [&](int st, lds_u8* __restrict__ buf) {
-    const bool comp = COMP && st < ncs;
+  // Past the last stage the ring keeps issuing (reloads of the last stage into a free buffer), so
+  // that every iteration has the same loads in flight and the same waits.
+  auto issue = [&](int st_req, lds_u8* __restrict__ buf, bool may_comp) {
+    const int st = min(st_req, nst - 1);
+    const bool comp = COMP && may_comp && st < ncs;
     if (comp) {
 #pragma unroll
       for (int i = 0; i < C::NIMAX; ++i) {
@@ -244,8 +238,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
 
   // prologue: NS-1 stages in flight
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nst) issue(s, smem + s * C::STAGE);
+  for (int s = 0; s < NS - 1; ++s) issue(s, smem + s * C::STAGE, true);
 
   int arow[C::TM], brow[C::TN];
 #pragma unroll
@@ -267,10 +260,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   auto lds4 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v4i*)p; };
   auto lds2 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v2i*)p; };
 
-  auto read_half = [&](int st, int hf, Frag& f) {
+  auto read_half = [&](int st, int hf, Frag& f, bool comp_stage) {
     const lds_u8* __restrict__ As = smem + (st % NS) * C::STAGE;
     const lds_u8* __restrict__ Bs = As + C::OFF_B;
-    if (COMP && st < ncs) {
+    if (COMP && comp_stage) {
       const bool valid = 32 * st + 16 * hf + 8 * h < K;  // chunks past K are zero operands
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
@@ -383,58 +376,64 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     }
   };
 
-  // Middle of stage st: wait for this wave's DMA of stage st+1, barrier (stage st+1 visible to
-  // all; stage st-1 no longer read by anyone), refill the freed buffer with stage st+NS-1.
-  auto middle = [&](int st) {
-    if (st + 1 < nst) {
-      const int pending = min(NS - 3, nst - 2 - st);  // stages issued after st+1
-      if (xside) wait_stage<NS - 3, C::DA>(pending);
-      else wait_stage<NS - 3, C::DB>(pending);
-    }
+  // One stage per iteration:
+  //   top     issue the DMA of stage st+NS-1 into the buffer freed at the previous barrier;
+  //           read the second half's operands of stage st;
+  //   half 0  MFMAs on operands read in the previous iteration;
+  //   middle  wait for this wave's DMA of stage st+1 (a wave with fewer loads per stage than
+  //           the other class over-waits, which is safe), barrier: stage st+1 is visible to all
+  //           and stage st is no longer read by anyone; read stage st+1's first-half operands;
+  //   half 1  MFMAs.
+  // Every MFMA then finds its operands in registers and the barrier is the only bubble.
+  constexpr int DMIN = C::DA < C::DB ? C::DA : C::DB;
+  auto middle = [&]() {
+    wait_vm<(NS - 2) * DMIN>();
     lds_barrier();
-    if (st + NS - 1 < nst) issue(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE);
   };
 
-  // Pipeline: the second half's operands are read before the first half's MFMAs, the next
-  // stage's first-half operands right after the mid-stage barrier, so that every MFMA finds its
-  // operands in registers and the barrier is the only bubble.  Two loops over the one ring keep
-  // one kind of MFMA per loop body.
   Frag f0, f1;
   Scales sc, scn;
-  {
-    const int pending = min(NS - 2, nst - 1);  // stages issued after stage 0
-    if (xside) wait_stage<NS - 2, C::DA>(pending);
-    else wait_stage<NS - 2, C::DB>(pending);
-  }
+  wait_vm<(NS - 2) * DMIN>();  // stage 0 complete for this wave
   lds_barrier();
-  read_half(0, 0, f0);
-  if (!(COMP && 0 < ncs)) read_scales(0, sc);
+  read_half(0, 0, f0, COMP && ncs > 0);
+  if (!(COMP && ncs > 0)) read_scales(0, sc);
 
   int st = 0;
   if constexpr (COMP) {
-    for (; st < ncs; ++st) {
-      read_half(st, 1, f1);
+    // all compensation stages but the last; the last one hands over to the first main stage
+    for (; st < ncs - 1; ++st) {
+      issue(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE, true);
+      read_half(st, 1, f1, true);
       mfma_comp(f0);
-      middle(st);
-      if (st + 1 < nst) {
-        read_half(st + 1, 0, f0);
-        if (st + 1 >= ncs) read_scales(st + 1, scn);
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      middle();
+      read_half(st + 1, 0, f0, true);
       mfma_comp(f1);
-      sc = scn;
+    }
+    if (ncs > 0) {
+      issue(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE, true);
+      read_half(st, 1, f1, true);
+      mfma_comp(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      middle();
+      read_half(st + 1, 0, f0, false);
+      read_scales(st + 1, sc);
+      mfma_comp(f1);
+      ++st;
     }
   }
   for (; st < nst; ++st) {
-    read_half(st, 1, f1);
+    issue(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE, false);
+    read_half(st, 1, f1, false);
     mfma_main(0, f0, sc);
-    middle(st);
-    if (st + 1 < nst) {
-      read_half(st + 1, 0, f0);
-      read_scales(st + 1, scn);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    middle();
+    read_half(st + 1, 0, f0, false);  // past the end: reads a reloaded buffer, unused
+    read_scales(st + 1, scn);
     mfma_main(1, f1, sc);
     sc = scn;
   }
+  wait_vm<0>();  // no LDS DMA may still be in flight when the workgroup ends
 
   // ---------------------------------------------------------------- epilogue
   auto store = [&](bool guard) {
