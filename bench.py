@@ -62,17 +62,18 @@ class Layer:
         S, H, N, G = w.S, w.H, w.N, w.G
         K = H // G
         self.S, self.H, self.N, self.G, self.L, self.afmt, self.wfmt = S, H, N, G, L, afmt, wfmt
-        cq = lambda n, f: (n, H // 2 if f == osc.OSC_MXFP4 else H)
         import numpy as np
+        u8 = lambda n: torch.empty((n,), dtype=torch.uint8, device=dev)
+        side = lambda R: torch.empty((osc.side_elems(R, H, G),), dtype=torch.int16, device=dev)
         self.X = X_dev if X_dev is not None else torch.from_numpy(w.X.view(np.int16)).to(dev)
-        self.QX = torch.empty(cq(S, afmt), dtype=torch.uint8, device=dev)
-        self.SX = torch.empty((S, K), dtype=torch.uint8, device=dev)
-        self.B = torch.empty((S, K), dtype=torch.int16, device=dev) if L is not None else None
+        self.QX = u8(osc.code_bytes(S, H, afmt))
+        self.SX = u8(osc.scale_bytes(S, H, G))
+        self.B = side(S) if L is not None else None
         if packed is None:
             Wd = torch.from_numpy(w.W.view(np.int16)).to(dev)
-            self.QW = torch.empty(cq(N, wfmt), dtype=torch.uint8, device=dev)
-            self.SW = torch.empty((N, K), dtype=torch.uint8, device=dev)
-            self.WL = torch.empty((N, K), dtype=torch.int16, device=dev) if L is not None else None
+            self.QW = u8(osc.code_bytes(N, H, wfmt))
+            self.SW = u8(osc.scale_bytes(N, H, G))
+            self.WL = side(N) if L is not None else None
             osc.osc_pack_weights(Wd, N, H, G, L, wfmt, self.QW, self.SW, self.WL)  # offline, untimed
             del Wd
         else:

@@ -18,13 +18,24 @@
  * rounds to zero keeps its sign bit; the zeroed outlier slot encodes as +0.
  *
  * Conventions shared by every call
- *   - bf16 tensors are raw IEEE bfloat16; all matrices are row-major, no padding.
- *   - X is S x H (tokens x input channels); W is N x H (PyTorch Linear: out x in).
+ *   - bf16 tensors are raw IEEE bfloat16.  X is S x H (tokens x input channels) and
+ *     W is N x H (PyTorch Linear: out x in), row-major; Y is S x N, row-major.
  *   - K = H / G groups per row; group k covers channels [k*G, (k+1)*G).
- *   - Element codes: MXFP4 packs two E2M1 codes per byte, element 2i in the low
- *     nibble of byte i (H/2 bytes per row); MXFP8 stores one E4M3 byte per element.
- *   - Scales: rows x K bytes of E8M0 (bias 127; 255 is never produced).
- *   - L: HOST array of K int32 entries in {-1} ∪ [0, G), read during the call and
+ *   - E8M0 scale bytes have bias 127; 255 is never produced.
+ *   - Quantized operands (QX, SX, B from osc_quant_act; QW, SW, WL from
+ *     osc_pack_weights) use one TILED layout, chosen so that the GEMM streams each
+ *     K-slice of a tile as one contiguous block.  With R rows (S or N):
+ *       codes   H/128 panels of R x CB bytes, CB = 64 (MXFP4) or 128 (MXFP8); the
+ *               codes of row r, channels [128p, 128p + 128) start at byte
+ *               (p*R + r)*CB.  Inside a panel row: MXFP4 packs two E2M1 codes per
+ *               byte, channel 2i (of the panel) in the low nibble of byte i; MXFP8
+ *               one E4M3 byte per channel.  H*R/2 or H*R bytes in all.
+ *       scales  panels of SPG groups, SPG = 8 when G = 16 and 4 otherwise: the scale
+ *               of row r, group k is byte (k/SPG * R + r)*SPG + k%SPG.  R*K bytes.
+ *       B, WL   panels of 32 groups: the bf16 of row r, group k is element
+ *               (k/32 * R + r)*32 + k%32; ceil(K/32)*32*R elements, those of groups
+ *               >= K are never written and never used.
+  *   - L: HOST array of K int32 entries in {-1} ∪ [0, G), read during the call and
  *     passed to the kernels by value (kernel arguments), so a call can be captured
  *     in a HIP graph; K <= OSC_MAX_GROUPS.
  *   - Every other pointer is DEVICE memory owned by the caller, 16-byte aligned.
@@ -76,13 +87,11 @@ typedef enum {
  *   W   [N][H] bf16, device.  Quantized unmodified along H in groups of G.
  *   L   host int32[K] table slice, or NULL (no compensation path: WL must be NULL).
  *   wfmt  OSC_MXFP4 or OSC_MXFP8.
- *   QW  [N][H/2] bytes (MXFP4) or [N][H] (MXFP8), device, written.
- *   SW  [N][K] E8M0 bytes, device, written.
- *   WL  [N][K] bf16, device, written: WL[n][k] = W[n][k*G + L[k]], or +0 when
- *       L[k] = -1.  This is the page's K x N slice W_L stored output-major (the
- *       layout of W itself), so every output channel's K compensation weights
- *       are contiguous.
- * Constraints: N >= 0, H > 0, G in {16, 32, 64}, H % G == 0, K <= OSC_MAX_GROUPS.
+ *   QW  element codes, tiled (R = N), device, written.
+ *   SW  E8M0 scales, tiled (R = N), device, written.
+ *   WL  bf16, tiled (R = N), device, written: WL(n, k) = W[n][k*G + L[k]], or +0
+ *       when L[k] = -1.  This is the page's K x N slice W_L stored output-major.
+ * Constraints: N >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS.
  */
 osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt,
                             void* QW, uint8_t* SW, void* WL, void* stream);
@@ -93,20 +102,20 @@ osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L
  *   L   host int32[K] table slice, or NULL: no extraction (direct MX quantization,
  *       and the FP8 fallback of §4); then B must be NULL.
  *   afmt  OSC_MXFP4 or OSC_MXFP8.
- *   QX  [S][H/2] (MXFP4) or [S][H] (MXFP8) bytes, device, written.
- *   SX  [S][K] E8M0 bytes, device, written; computed on the zeroed group.
- *   B   [S][K] bf16, device, written: B[s][k] = X[s][k*G + L[k]] bit for bit, or
- *       +0 when L[k] = -1.
- * Constraints: S >= 0, H > 0, G in {16, 32, 64}, H % G == 0, K <= OSC_MAX_GROUPS.
+ *   QX  element codes, tiled (R = S), device, written.
+ *   SX  E8M0 scales, tiled (R = S), device, written; computed on the zeroed group.
+ *   B   bf16, tiled (R = S), device, written: B(s, k) = X[s][k*G + L[k]] bit for
+ *       bit, or +0 when L[k] = -1.
+ * Constraints: S >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS.
  */
 osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt,
                          void* QX, uint8_t* SX, void* B, void* stream);
 
 /*
  * osc_gemm -- the dual-path OSC product (§3.2):
- *   Y[s][n] = sum_k 2^(eX[s][k] + eW[n][k]) * sum_{j<G} qX[s][kG+j] * qW[n][kG+j]
- *           + sum_k B[s][k] * WL[n][k]
- * with MXFP4 operands from osc_quant_act / osc_pack_weights, accumulated in
+ *   Y[s][n] = sum_k 2^(eX(s,k) + eW(n,k)) * sum_{j<G} qX(s,kG+j) * qW(n,kG+j)
+ *           + sum_k B(s,k) * WL(n,k)
+ * with tiled MXFP4 operands from osc_quant_act / osc_pack_weights, accumulated in
  * fp32 (each 4-bit product and each bf16 product is exact in fp32).  The 16-bit
  * compensation runs in the same kernel, into the same fp32 accumulators.
  *   B, WL  both NULL for a plain MXFP4 GEMM (no compensation), else both set.
@@ -120,7 +129,7 @@ osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void
 
 /*
  * osc_gemm_fp8 -- the W2 fallback of §4: Y = (QX8 ⊗ QW)·S with E4M3 activations
- * (osc_quant_act with afmt = OSC_MXFP8, L = NULL) and weights in wfmt (OSC_MXFP4,
+ * (tiled, from osc_quant_act with afmt = OSC_MXFP8, L = NULL) and weights in wfmt (OSC_MXFP4,
  * the default W4A8 reading, or OSC_MXFP8); no extraction, no compensation.
  *   Y   [S][N], bf16 or fp32 per yt, device, written.
  * Constraints: S >= 0, N >= 0, G in {32, 64}, H % 256 == 0, K <= OSC_MAX_GROUPS.
@@ -131,7 +140,7 @@ osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, cons
 
 /*
  * osc_build_table -- offline suppression-table slice for one (position, layer)
- * (§3.1, Algorithm 1), from R calibration rows Xcal [R][H] bf16 (device).
+ * (§3.1, Algorithm 1), from R calibration rows Xcal [R][H] bf16 (device, row-major).
  * find_consistent_outlier is only named on the page; this library reads it as:
  * a row is an outlier event in group k when the group's largest |x| exceeds
  * alpha times the group's mean |x| (compared in fp64), its channel being the

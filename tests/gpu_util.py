@@ -1,6 +1,10 @@
 """Test-side helpers: move seeded numpy inputs to the GPU, run the libosc calls through the
 Python binding, and compare against the oracle.  Outputs are pre-filled with 0xFF bytes
-so that an unwritten element cannot pass a bit-exact comparison by accident."""
+so that an unwritten element cannot pass a bit-exact comparison by accident.
+
+libosc's quantized operands use the tiled layout of include/osc.h; the oracle's are
+row-major.  The ``*_rm`` helpers undo the tiling on the host (a pure permutation) so
+the two compare element by element."""
 import numpy as np
 import torch
 
@@ -36,22 +40,48 @@ def code_cols(H: int, fmt: int) -> int:
     return H // 2 if fmt == osc.OSC_MXFP4 else H
 
 
+def _tiled_outputs(R: int, H: int, G: int, fmt: int, with_side: bool):
+    Q = poisoned((osc.code_bytes(R, H, fmt),), torch.uint8)
+    SC = poisoned((osc.scale_bytes(R, H, G),), torch.uint8)
+    side = poisoned((osc.side_elems(R, H, G),), torch.int16) if with_side else None
+    return Q, SC, side
+
+
 def quant(X_dev: torch.Tensor, S: int, H: int, G: int, L, fmt: int):
-    K = H // G
-    QX = poisoned((S, code_cols(H, fmt)), torch.uint8)
-    SX = poisoned((S, K), torch.uint8)
-    B = poisoned((S, K), torch.int16) if L is not None else None
+    """-> tiled device buffers (QX, SX, B or None)."""
+    QX, SX, B = _tiled_outputs(S, H, G, fmt, L is not None)
     osc.osc_quant_act(X_dev, S, H, G, L, fmt, QX, SX, B)
     return QX, SX, B
 
 
 def pack(W_dev: torch.Tensor, N: int, H: int, G: int, L, fmt: int):
-    K = H // G
-    QW = poisoned((N, code_cols(H, fmt)), torch.uint8)
-    SW = poisoned((N, K), torch.uint8)
-    WL = poisoned((N, K), torch.int16) if L is not None else None
+    """-> tiled device buffers (QW, SW, WL or None)."""
+    QW, SW, WL = _tiled_outputs(N, H, G, fmt, L is not None)
     osc.osc_pack_weights(W_dev, N, H, G, L, fmt, QW, SW, WL)
     return QW, SW, WL
+
+
+def codes_rm(t: torch.Tensor, R: int, H: int, fmt: int) -> np.ndarray:
+    """tiled codes -> uint8[R, H/2 or H] row-major (panels of 128 channels)."""
+    cb = 64 if fmt == osc.OSC_MXFP4 else 128
+    a = host_u8(t).reshape(H // 128, R, cb)
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(R, (H // 128) * cb))
+
+
+def scales_rm(t: torch.Tensor, R: int, H: int, G: int) -> np.ndarray:
+    """tiled E8M0 scales -> uint8[R, K] row-major (panels of 8 groups for G=16, else 4)."""
+    K = H // G
+    spg = 8 if G == 16 else 4
+    a = host_u8(t).reshape(K // spg, R, spg)
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(R, K))
+
+
+def side_rm(t: torch.Tensor, R: int, H: int, G: int) -> np.ndarray:
+    """tiled B / W_L -> uint16 bf16 bits [R, K] row-major (panels of 32 groups)."""
+    K = H // G
+    kp = (K + 31) // 32
+    a = host_bits16(t).reshape(kp, R, 32)
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(R, kp * 32)[:, :K])
 
 
 def gemm(QX, SX, B, QW, SW, WL, S, N, H, G, yt=osc.OSC_Y_F32):

@@ -52,6 +52,7 @@ def test_quant_act_validation():
     assert q(f=7) == 5                      # bad format
     assert q(G=8) == 2 and q(G=128) == 2     # G not in {16, 32, 64}
     assert q(H=250) == 2                     # H % G != 0
+    assert q(H=384) == 2                     # tiled layout: H % 256 != 0
     assert q(S=-1) == 2
     assert q(X=None) == 1 and q(QX=None) == 1 and q(SX=None) == 1
     assert q(B=None) == 1                    # table given but no B
@@ -71,6 +72,7 @@ def test_pack_weights_validation():
     assert p(WL=None) == 1 and p(l=None) == 1
     assert p(W=U) == 4 and p(SW=U) == 4
     assert p(N=-3) == 2
+    assert p(H=384) == 2
     bad, bp = L8([3, 3, 3, 3, 3, 3, 3, 40])
     assert p(l=bp) == 3
 

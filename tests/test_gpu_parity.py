@@ -21,8 +21,8 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import w4a4_outlier_split_amd as osc  # noqa: E402  (loud ImportError when the library is missing)
-from gpu_util import (assert_y_close, dev_bits16, gemm, gemm_fp8, host_bits16, host_u8, host_y, pack,  # noqa: E402
-                      quant)
+from gpu_util import (assert_y_close, codes_rm, dev_bits16, gemm, gemm_fp8, host_y, pack, quant,  # noqa: E402
+                      scales_rm, side_rm)
 
 FP4, FP8 = osc.OSC_MXFP4, osc.OSC_MXFP8
 
@@ -77,10 +77,10 @@ def test_quant_exhaustive_bf16(G, fmt):
     QX, SX, B = quant(dev_bits16(X), S, H, G, L, fmt)
     torch.cuda.synchronize()
     rq, rs, rb = oracle.quant_act(X, G, L, fmt)
-    np.testing.assert_array_equal(host_u8(SX), rs)
-    np.testing.assert_array_equal(host_u8(QX), rq)
+    np.testing.assert_array_equal(scales_rm(SX, S, H, G), rs)
+    np.testing.assert_array_equal(codes_rm(QX, S, H, fmt), rq)
     if L is not None:
-        np.testing.assert_array_equal(host_bits16(B), rb)
+        np.testing.assert_array_equal(side_rm(B, S, H, G), rb)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qkv", "gsweep_8192_16", "gsweep_2048_64"])
@@ -90,9 +90,9 @@ def test_quant_workloads_mxfp4(name):
     QX, SX, B = quant(dev_bits16(w.X), w.S, w.H, w.G, L, FP4)
     torch.cuda.synchronize()
     rq, rs, rb = oracle.quant_act(w.X, w.G, L, FP4)
-    np.testing.assert_array_equal(host_u8(SX), rs)
-    np.testing.assert_array_equal(host_bits16(B), rb)
-    np.testing.assert_array_equal(host_u8(QX), rq)
+    np.testing.assert_array_equal(scales_rm(SX, w.S, w.H, w.G), rs)
+    np.testing.assert_array_equal(side_rm(B, w.S, w.H, w.G), rb)
+    np.testing.assert_array_equal(codes_rm(QX, w.S, w.H, FP4), rq)
 
 
 def test_quant_down_proj_mxfp8():
@@ -101,21 +101,23 @@ def test_quant_down_proj_mxfp8():
     torch.cuda.synchronize()
     rows = sample_rows(w.S, 512, 1)
     rq, rs, _ = oracle.quant_act(w.X[rows], w.G, None, FP8)
-    np.testing.assert_array_equal(host_u8(SX)[rows], rs)
-    np.testing.assert_array_equal(host_u8(QX)[rows], rq)
+    np.testing.assert_array_equal(scales_rm(SX, w.S, w.H, w.G)[rows], rs)
+    np.testing.assert_array_equal(codes_rm(QX, w.S, w.H, FP8)[rows], rq)
 
 
 def test_quant_ragged_and_empty():
-    X = synth.random_bf16((37, 96), seed=5, scale=3.0)
-    L = np.array([5, -1, 0, 15, 15, -1], np.int32)
-    for G, Lg in ((16, L), (32, L[:3]), (32, None)):
-        QX, SX, B = quant(dev_bits16(X), 37, 96, G, Lg, FP4)
+    """37 rows (no tile multiple), K = 4 .. 16 groups (scale panels, a partial B panel)."""
+    S, H = 37, 256
+    X = synth.random_bf16((S, H), seed=5, scale=3.0)
+    L = np.array([5, -1, 0, 15, 15, -1, 3, 3, 0, 1, 2, -1, 7, 8, 9, 10], np.int32)
+    for G, Lg, fmt in ((16, L, FP4), (32, L[:8], FP4), (32, None, FP4), (64, L[:4], FP4), (64, None, FP8)):
+        QX, SX, B = quant(dev_bits16(X), S, H, G, Lg, fmt)
         torch.cuda.synchronize()
-        rq, rs, rb = oracle.quant_act(X, G, Lg, FP4)
-        np.testing.assert_array_equal(host_u8(QX), rq)
-        np.testing.assert_array_equal(host_u8(SX), rs)
+        rq, rs, rb = oracle.quant_act(X, G, Lg, fmt)
+        np.testing.assert_array_equal(codes_rm(QX, S, H, fmt), rq)
+        np.testing.assert_array_equal(scales_rm(SX, S, H, G), rs)
         if Lg is not None:
-            np.testing.assert_array_equal(host_bits16(B), rb)
+            np.testing.assert_array_equal(side_rm(B, S, H, G), rb)
     # S = 0: valid, launches nothing
     empty = torch.empty((0, 256), dtype=torch.int16, device="cuda:0")
     osc.osc_quant_act(empty, 0, 256, 32, None, FP4, empty, empty, None)
@@ -132,9 +134,9 @@ def test_pack_weights(name, fmt):
     torch.cuda.synchronize()
     rows = sample_rows(w.N, 1024, 2)
     rq, rs, rwl = oracle.pack_weights(w.W[rows], w.G, L, fmt)
-    np.testing.assert_array_equal(host_u8(SW)[rows], rs)
-    np.testing.assert_array_equal(host_u8(QW)[rows], rq)
-    np.testing.assert_array_equal(host_bits16(WL)[rows], rwl)
+    np.testing.assert_array_equal(scales_rm(SW, w.N, w.H, w.G)[rows], rs)
+    np.testing.assert_array_equal(codes_rm(QW, w.N, w.H, fmt)[rows], rq)
+    np.testing.assert_array_equal(side_rm(WL, w.N, w.H, w.G)[rows], rwl)
 
 
 # ------------------------------------------------------------------ table builder
@@ -248,7 +250,7 @@ def test_all_minus_one_table_is_plain_mxfp4():
     L = np.full(w.H // w.G, -1, np.int32)
     QX, SX, B = quant(dev_bits16(w.X), w.S, w.H, w.G, L, FP4)
     QW, SW, WL = pack(dev_bits16(w.W), w.N, w.H, w.G, L, FP4)
-    assert torch.all(B == 0) and torch.all(WL == 0)
+    assert np.all(side_rm(B, w.S, w.H, w.G) == 0) and np.all(side_rm(WL, w.N, w.H, w.G) == 0)
     Y1 = gemm(QX, SX, B, QW, SW, WL, w.S, w.N, w.H, w.G)
     QX2, SX2, _ = quant(dev_bits16(w.X), w.S, w.H, w.G, None, FP4)
     assert torch.equal(QX, QX2) and torch.equal(SX, SX2)

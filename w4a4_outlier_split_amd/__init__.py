@@ -56,6 +56,21 @@ _lib.osc_last_device_error.argtypes = []
 _lib.osc_last_device_error.restype = ctypes.c_char_p
 
 
+def code_bytes(rows: int, H: int, fmt: int) -> int:
+    """Bytes of a tiled code buffer (QX / QW) for ``rows`` rows of H channels."""
+    return rows * (H // 2 if fmt == OSC_MXFP4 else H)
+
+
+def scale_bytes(rows: int, H: int, G: int) -> int:
+    """Bytes of a tiled E8M0 scale buffer (SX / SW): one per row and group."""
+    return rows * (H // G)
+
+
+def side_elems(rows: int, H: int, G: int) -> int:
+    """bf16 elements of a tiled B / W_L buffer: panels of 32 groups, the last one padded."""
+    return rows * ((H // G + 31) // 32) * 32
+
+
 class OscError(RuntimeError):
     def __init__(self, status: int, call: str):
         self.status = status

@@ -19,6 +19,13 @@ osc_status check_dims(int rows, int H, int G) {
   return OSC_OK;
 }
 
+// shapes of the tiled operand layout: whole 128-channel code panels and whole scale panels
+osc_status check_tiled(int rows, int H, int G) {
+  const osc_status st = check_dims(rows, H, G);
+  if (st != OSC_OK) return st;
+  return H % 256 == 0 ? OSC_OK : OSC_E_SHAPE;
+}
+
 // copy the host table slice into the kernel-argument struct, checking every entry
 osc_status pack_table(const int32_t* L, int K, int G, osc::TableArg* t) {
   for (int k = 0; k < K; ++k) {
@@ -63,7 +70,7 @@ const char* osc_last_device_error(void) {
 osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt, void* QX, uint8_t* SX,
                          void* B, void* stream) {
   if (afmt != OSC_MXFP4 && afmt != OSC_MXFP8) return OSC_E_FORMAT;
-  osc_status st = check_dims(S, H, G);
+  osc_status st = check_tiled(S, H, G);
   if (st != OSC_OK) return st;
   if (S == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
   if (!X || !QX || !SX) return OSC_E_NULL;
@@ -81,7 +88,7 @@ osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, o
 osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt, void* QW, uint8_t* SW,
                             void* WL, void* stream) {
   if (wfmt != OSC_MXFP4 && wfmt != OSC_MXFP8) return OSC_E_FORMAT;
-  osc_status st = check_dims(N, H, G);
+  osc_status st = check_tiled(N, H, G);
   if (st != OSC_OK) return st;
   if (N == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
   if (!W || !QW || !SW) return OSC_E_NULL;

@@ -165,10 +165,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   // [64q, 64q+64) of its region; lane l -> chunk p = 64q + l.
   const bool xside = wave < C::NCW;
   const int cw = xside ? wave : wave - C::NCW;
-  const int rb_g = xside ? (FA == kFp4 ? H / 2 : H) : (FB == kFp4 ? H / 2 : H);   // global row bytes
-  const int rb_l = xside ? C::RBA : C::RBB;                                        // LDS row bytes
+  const int rb_l = xside ? C::RBA : C::RBB;  // bytes per row per code panel (64 E2M1, 128 E4M3)
   const int r0 = xside ? m0 : n0;
-  const int rmax = (xside ? S : N) - 1;
+  const int R = xside ? S : N;               // rows of this side's operands
+  const int rmax = R - 1;
   const uint8_t* const gcodes = xside ? QX : QW;
   const uint8_t* const gcomp = xside ? Bc : WL;
   const uint8_t* const gscale = xside ? SX : SW;
@@ -176,9 +176,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   const int nsc = xside ? C::SCA : C::SCB;
   const int dst_rows = xside ? 0 : C::OFF_B;
   const int dst_scale = xside ? C::OFF_SA : C::OFF_SB;
+  // Operands arrive in the tiled layout: a stage of a tile is one contiguous R-major block of
+  // every panel (codes: rb_l bytes per row; B / W_L: 64 bytes = 32 groups per row; scales: SBL
+  // bytes per row), so every DMA instruction covers whole cache lines.
+  const long code_panel = (long)R * rb_l;
+  const long comp_panel = (long)R * 64;
+  const long scale_panel = (long)R * C::SBL;
   const uint8_t* src[C::NIMAX];
   const uint8_t* srcC[COMP ? C::NIMAX : 1];
-  int ccv[C::NIMAX];
 #pragma unroll
   for (int i = 0; i < C::NIMAX; ++i) {
     const int p = (C::NCW * i + cw) * 64 + lane;
@@ -187,9 +192,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const int pc = p % cpr;
     const int cc = rb_l == 64 ? swz<64>(r, pc) : swz<128>(r, pc);
     const long gr = min(r0 + r, rmax);  // ragged edge: clamped rows are never stored
-    src[i] = gcodes + gr * rb_g + cc * 16;
-    ccv[i] = cc;
-    if constexpr (COMP) srcC[i] = gcomp + gr * (2L * K);
+    src[i] = gcodes + gr * rb_l + cc * 16;
+    if constexpr (COMP) srcC[i] = gcomp + gr * 64 + cc * 16;
   }
   // scale bytes: lane l of wave-instruction q covers row q*SRPI + l/SLPR, bytes 4*(l%SLPR)
   const uint8_t* srcS[C::SCMAX];
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   for (int i = 0; i < C::SCMAX; ++i) {
     const int q = C::NCW * i + cw;
     const int r = q * C::SRPI + lane / C::SLPR;
-    srcS[i] = gscale + (long)min(r0 + r, rmax) * K + (lane % C::SLPR) * 4;
+    srcS[i] = gscale + (long)min(r0 + r, rmax) * C::SBL + (lane % C::SLPR) * 4;
   }
 
   // Past the last stage the ring keeps issuing (reloads of the last stage into a free buffer), so
@@ -206,23 +210,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const int st = min(st_req, nst - 1);
     const bool comp = COMP && may_comp && st < ncs;
     if (comp) {
+      // compensation panel st; groups past K (last panel) are loaded and zeroed at use
+      const long off = (long)st * comp_panel;
 #pragma unroll
-      for (int i = 0; i < C::NIMAX; ++i) {
-        if (i < ni) {
-          const bool ok = 32 * st + 8 * ccv[i] < K;  // chunks past K: any valid address, zeroed at use
-          dma16(srcC[COMP ? i : 0] + (ok ? 64 * st + 16 * ccv[i] : 0), buf + dst_rows + (C::NCW * i + cw) * 1024);
-        }
-      }
+      for (int i = 0; i < C::NIMAX; ++i)
+        if (i < ni) dma16(srcC[COMP ? i : 0] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
     } else {
-      const long off = (long)(st - ncs) * rb_l;
+      const long off = (long)(st - ncs) * code_panel;
 #pragma unroll
       for (int i = 0; i < C::NIMAX; ++i)
         if (i < ni) dma16(src[i] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
     }
     // scales (also issued for compensation stages, from stage 0, so every stage has the same
-    // number of loads per wave)
+    // number of loads per wave); with G=64 one scale panel serves two stages
     const int ks = comp ? 0 : st - ncs;
-    const int soff = C::SB >= 4 ? ks * C::SB : (ks >> 1) * 4;
+    const long soff = (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel;
 #pragma unroll
     for (int i = 0; i < C::SCMAX; ++i)
       if (i < nsc) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);

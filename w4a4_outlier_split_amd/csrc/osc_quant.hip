@@ -4,7 +4,9 @@
 // copied into the contiguous W_L block without zeroing).
 //
 // Data flow: HBM-bound.  Each lane owns one 16-byte chunk (8 bf16) of a row, so a wavefront
-// reads 1 KiB of consecutive memory and G/8 adjacent lanes form one group.  The group amax is
+// reads 1 KiB of consecutive memory and G/8 adjacent lanes form one group.  Outputs go to the
+// tiled layout the GEMM streams: codes in panels of 128 channels (R rows x 64 or 128 bytes),
+// scales in panels of 4 groups (8 when G = 16), B / W_L in panels of 32 groups.  The group amax is
 // an integer max over the bf16 magnitude bits (|x| ordering == bit ordering for finite values),
 // reduced across the group's lanes with cross-lane swizzles.  The E8M0 code is read straight
 // off the amax exponent field: floor(log2 amax) - emax + 127 = E - 2 (E2M1) or E - 8 (E4M3),
@@ -28,7 +30,7 @@ __device__ __forceinline__ uint32_t as_u32(us2 v) { return __builtin_bit_cast(ui
 __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
 
 template <int G, int FMT, int MODE>
-__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nchunks, int H, TableArg tab,
+__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nchunks, int rows, int H, TableArg tab,
                                                uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
                                                uint16_t* __restrict__ side) {
   constexpr int LPG = G / 8;  // lanes per group
@@ -41,7 +43,10 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nc
   const int col0 = (int)(c - r * cpr) << 3;
   const int k = col0 / G;
   const int q = (col0 % G) >> 3;
-  const int K = H / G;
+  constexpr int SPG = G == 16 ? 8 : 4;  // groups per scale panel
+  const long code_at = ((long)(col0 >> 7) * rows + r) * 16 + ((col0 & 127) >> 3);  // in 4 / 8-byte units
+  const long scale_at = ((long)(k / SPG) * rows + r) * SPG + k % SPG;
+  const long side_at = ((long)(k >> 5) * rows + r) * 32 + (k & 31);
 
   const u4 v = __builtin_nontemporal_load(X + c);
   uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nc
         w3 = (e >> 1) == 3 ? (w3 & keep) : w3;
       }
     }
-    if (own || (ent < 0 && q == 0)) side[r * K + k] = (uint16_t)val;
+    if (own || (ent < 0 && q == 0)) side[side_at] = (uint16_t)val;
   }
 
   // group amax over the magnitude bits
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nc
   }
   const int E = amax >> 7;
   const int sx = FMT == OSC_MXFP4 ? (E > 2 ? E - 2 : 0) : (E > 8 ? E - 8 : 0);
-  if (q == 0) SC[r * K + k] = (uint8_t)sx;
+  if (q == 0) SC[scale_at] = (uint8_t)sx;
   const float scale = __builtin_bit_cast(float, (uint32_t)sx << 23);  // only the exponent field is used
 
   if (FMT == OSC_MXFP4) {
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nc
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w1), scale, 1);
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w2), scale, 2);
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w3), scale, 3);
-    __builtin_nontemporal_store(out, reinterpret_cast<uint32_t*>(Q) + c);
+    __builtin_nontemporal_store(out, reinterpret_cast<uint32_t*>(Q) + code_at);
   } else {
     // saturate: |x| <= 448 * 2^e, i.e. exponent field sx + 8 with mantissa 0b1100000
     const uint32_t lim = (((uint32_t)sx + 8u) << 7) | 0x60u;
@@ -101,12 +106,12 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nc
     o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, as_bf2(w2), scale, false);
     o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, as_bf2(w3), scale, true);
     const u2 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1)};
-    __builtin_nontemporal_store(o, reinterpret_cast<u2*>(Q) + c);
+    __builtin_nontemporal_store(o, reinterpret_cast<u2*>(Q) + code_at);
   }
 }
 
 template <int G, int FMT>
-hipError_t dispatch_mode(const void* X, long nchunks, int H, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+hipError_t dispatch_mode(const void* X, long nchunks, int rows, int H, const TableArg* tab, int mode, void* Q, uint8_t* SC,
                          void* side, hipStream_t st) {
   const unsigned grid = (unsigned)((nchunks + 255) / 256);
   const u4* x = static_cast<const u4*>(X);
@@ -115,19 +120,19 @@ hipError_t dispatch_mode(const void* X, long nchunks, int H, const TableArg* tab
   static const TableArg empty = {};
   const TableArg& t = tab ? *tab : empty;
   if (mode == kExtractZero)
-    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, nchunks, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, nchunks, rows, H, t, q, SC, sd);
   else if (mode == kCopyOnly)
-    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, nchunks, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, nchunks, rows, H, t, q, SC, sd);
   else
-    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, nchunks, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, nchunks, rows, H, t, q, SC, sd);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t dispatch_fmt(const void* X, long nchunks, int H, const TableArg* tab, int mode, osc_fmt fmt, void* Q,
-                        uint8_t* SC, void* side, hipStream_t st) {
-  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, nchunks, H, tab, mode, Q, SC, side, st);
-  return dispatch_mode<G, OSC_MXFP8>(X, nchunks, H, tab, mode, Q, SC, side, st);
+hipError_t dispatch_fmt(const void* X, long nchunks, int rows, int H, const TableArg* tab, int mode, osc_fmt fmt,
+                        void* Q, uint8_t* SC, void* side, hipStream_t st) {
+  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, nchunks, rows, H, tab, mode, Q, SC, side, st);
+  return dispatch_mode<G, OSC_MXFP8>(X, nchunks, rows, H, tab, mode, Q, SC, side, st);
 }
 
 // ------------------------------------------------------------------ table builder
@@ -184,9 +189,9 @@ hipError_t launch_quant(const void* X, int rows, int H, int G, const TableArg* t
   const long nchunks = (long)rows * (H / 8);
   if (nchunks == 0) return hipSuccess;
   switch (G) {
-    case 16: return dispatch_fmt<16>(X, nchunks, H, tab, mode, fmt, Q, SC, side, st);
-    case 32: return dispatch_fmt<32>(X, nchunks, H, tab, mode, fmt, Q, SC, side, st);
-    default: return dispatch_fmt<64>(X, nchunks, H, tab, mode, fmt, Q, SC, side, st);
+    case 16: return dispatch_fmt<16>(X, nchunks, rows, H, tab, mode, fmt, Q, SC, side, st);
+    case 32: return dispatch_fmt<32>(X, nchunks, rows, H, tab, mode, fmt, Q, SC, side, st);
+    default: return dispatch_fmt<64>(X, nchunks, rows, H, tab, mode, fmt, Q, SC, side, st);
   }
 }
 
