@@ -11,7 +11,10 @@ steps rotate over buffer sets whose total exceeds the 256 MB Infinity Cache.
 
 metric: TFLOP/s = 2*S*H*N / (t_quant + t_gemm), from the wall clock of K steps
 bracketed by device synchronisation.  The GEMM's average kernel duration is measured
-with HIP events on the stream the kernels run on, for the roofline object.  The CPU
+with HIP events on the stream the kernels run on, for the roofline object.  Those events
+are created with hipEventDisableSystemFence: a default event's system-scope release
+writes the L2 back to memory when it is recorded, which would be charged to the kernels
+around it (and to the step).  The CPU
 baseline is the oracle (test infrastructure) timed on a bounded row sample.
 
 Prints ONE JSON line.  Extra per-workload rows (FFN prefill / decode, W2 FP8 fallback,
@@ -87,6 +90,41 @@ class Layer:
                                                           self.WL, self.Y) if t is not None)
 
 
+class TimingEvents:
+    """HIP events without the system-scope fence, on the HIP runtime torch has loaded."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")  # already loaded by torch: same runtime
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            self._ok(self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE), "create")
+            self.ev.append(h)
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"hipEvent{what} failed: {rc}")
+
+    def record(self, i, stream_handle):
+        self._ok(self.hip.hipEventRecord(self.ev[i], stream_handle), "Record")
+
+    def ms(self, i, j):
+        t = self.ct.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self.ct.byref(t), self.ev[i], self.ev[j]), "ElapsedTime")
+        return t.value
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
 def time_layer(torch, osc, sets, steps, warmup, stream):
     """Run quant + GEMM over rotating buffer sets.  Returns wall seconds per step and the
     average event-timed durations of the quant and GEMM kernels inside the timed region."""
@@ -110,20 +148,21 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
             l = sets[i % len(sets)]
             quant(l)
             gemm(l)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+        ev = TimingEvents(2 * steps + 1)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             l = sets[i % len(sets)]
-            ev[3 * i].record(stream)
+            ev.record(2 * i, s)
             quant(l)
-            ev[3 * i + 1].record(stream)
+            ev.record(2 * i + 1, s)
             gemm(l)
-            ev[3 * i + 2].record(stream)
+        ev.record(2 * steps, s)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-    tq = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps * 1e-3
-    tg = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps * 1e-3
+    tq = sum(ev.ms(2 * i, 2 * i + 1) for i in range(steps)) / steps * 1e-3
+    tg = sum(ev.ms(2 * i + 1, 2 * i + 2) for i in range(steps)) / steps * 1e-3
+    ev.close()
     return (t1 - t0) / steps, tq, tg
 
 

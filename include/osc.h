@@ -91,7 +91,8 @@ typedef enum {
  *   SW  E8M0 scales, tiled (R = N), device, written.
  *   WL  bf16, tiled (R = N), device, written: WL(n, k) = W[n][k*G + L[k]], or +0
  *       when L[k] = -1.  This is the page's K x N slice W_L stored output-major.
- * Constraints: N >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS.
+ * Constraints: N >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS,
+ * N * H < 2^34.
  */
 osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt,
                             void* QW, uint8_t* SW, void* WL, void* stream);
@@ -106,7 +107,8 @@ osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L
  *   SX  E8M0 scales, tiled (R = S), device, written; computed on the zeroed group.
  *   B   bf16, tiled (R = S), device, written: B(s, k) = X[s][k*G + L[k]] bit for
  *       bit, or +0 when L[k] = -1.
- * Constraints: S >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS.
+ * Constraints: S >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS,
+ * S * H < 2^34.
  */
 osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt,
                          void* QX, uint8_t* SX, void* B, void* stream);

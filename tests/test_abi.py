@@ -53,6 +53,7 @@ def test_quant_act_validation():
     assert q(G=8) == 2 and q(G=128) == 2     # G not in {16, 32, 64}
     assert q(H=250) == 2                     # H % G != 0
     assert q(H=384) == 2                     # tiled layout: H % 256 != 0
+    assert q(S=1 << 22, H=4096) == 2         # S * H >= 2^34
     assert q(S=-1) == 2
     assert q(X=None) == 1 and q(QX=None) == 1 and q(SX=None) == 1
     assert q(B=None) == 1                    # table given but no B

@@ -23,6 +23,7 @@ osc_status check_dims(int rows, int H, int G) {
 osc_status check_tiled(int rows, int H, int G) {
   const osc_status st = check_dims(rows, H, G);
   if (st != OSC_OK) return st;
+  if ((long long)rows * (H / 8) > 0x7FFFFFFFLL) return OSC_E_SHAPE;  // 16-byte chunks indexed in 32 bits
   return H % 256 == 0 ? OSC_OK : OSC_E_SHAPE;
 }
 

@@ -43,6 +43,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kFp4 = 4;  // scaled-MFMA format codes
@@ -69,6 +71,24 @@ __device__ __forceinline__ void wait_vm() {
 // Workgroup barrier that orders LDS only: no vmcnt wait (the DMA ring keeps loads in flight
 // across it); the memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Instruction-scheduling recipe for one half-stage: NM MFMAs, each followed by (up to) one of
+// the NV loads into the LDS ring and a share of the ND LDS fragment reads, so that loads and
+// reads are issued between matrix instructions instead of in a burst that stalls them.
+template <int K, int NM, int NV, int ND>
+struct Interleave {
+  __device__ __forceinline__ static void run() {
+    if constexpr (K < NM) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if constexpr (K < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM load
+      constexpr int d = (ND * (K + 1)) / NM - (ND * K) / NM;
+      if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);  // d LDS reads
+      Interleave<K + 1, NM, NV, ND>::run();
+    } else if constexpr (NV > NM) {
+      __builtin_amdgcn_sched_group_barrier(0x020, NV - NM, 0);
+    }
+  }
+};
 
 __device__ __forceinline__ void dma16(const void* g, lds_u8* __restrict__ l) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
@@ -227,6 +247,32 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const long soff = (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel;
 #pragma unroll
     for (int i = 0; i < C::SCMAX; ++i)
+      if (i < nsc) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);
+  };
+
+  // Main-loop loads in two parts: the slots both DMA classes have (the first NIU code rows and
+  // SCU scale rows) go between the MFMAs of the first half-stage; the extra slots of the larger
+  // class follow in a small branch of their own.
+  constexpr int NIU = C::NIA < C::NIB ? C::NIA : C::NIB;
+  constexpr int SCU = C::SCA < C::SCB ? C::SCA : C::SCB;
+  auto issue_main_uniform = [&](int st_req, lds_u8* __restrict__ buf) {
+    const int ks = min(st_req, nst - 1) - ncs;
+    const long off = (long)ks * code_panel;
+#pragma unroll
+    for (int i = 0; i < NIU; ++i) dma16(src[i] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
+    const long soff = (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel;
+#pragma unroll
+    for (int i = 0; i < SCU; ++i) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);
+  };
+  auto issue_main_extra = [&](int st_req, lds_u8* __restrict__ buf) {
+    const int ks = min(st_req, nst - 1) - ncs;
+    const long off = (long)ks * code_panel;
+#pragma unroll
+    for (int i = NIU; i < C::NIMAX; ++i)
+      if (i < ni) dma16(src[i] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
+    const long soff = (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel;
+#pragma unroll
+    for (int i = SCU; i < C::SCMAX; ++i)
       if (i < nsc) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);
   };
 
@@ -424,20 +470,81 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
       ++st;
     }
   }
+  // The first half-stage's MFMAs have no use before the barrier, so the optimizer would sink
+  // them past it; an empty asm that takes the accumulators keeps them ahead of it.
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+  };
+  // per half-stage: MFMAs, LDS fragment reads (E4M3 rows take two per fragment; G=16 one 8-byte
+  // read per fragment and MFMA), scale reads, uniform loads
+  constexpr int NM_H = C::TM * C::TN * NSH;
+  constexpr int ND_H = (C::TM * (FA == kFp8 ? 2 : 1) + C::TN * (FB == kFp8 ? 2 : 1)) * NSH;
+  constexpr int NV_H = NIU + SCU;
   for (; st < nst; ++st) {
-    issue(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE, false);
+    lds_u8* const nb = smem + ((st + NS - 1) % NS) * C::STAGE;
+    issue_main_uniform(st + NS - 1, nb);
     read_half(st, 1, f1, false);
     mfma_main(0, f0, sc);
+    Interleave<0, NM_H, NV_H, ND_H>::run();
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);
+    issue_main_extra(st + NS - 1, nb);
     middle();
     read_half(st + 1, 0, f0, false);  // past the end: reads a reloaded buffer, unused
     read_scales(st + 1, scn);
     mfma_main(1, f1, sc);
+    Interleave<0, NM_H, 0, ND_H + C::TM + C::TN>::run();
     sc = scn;
   }
   wait_vm<0>();  // no LDS DMA may still be in flight when the workgroup ends
 
   // ---------------------------------------------------------------- epilogue
+  if constexpr (YT == OSC_Y_BF16) {
+    if ((N & 7) == 0) {
+      // bf16 through LDS: each wave packs its accumulators into a row-major tile image
+      // (neighbouring lanes trade one value so every lane writes a dword of two adjacent
+      // columns), then the workgroup writes whole 16-byte row chunks, i.e. full cache lines.
+      constexpr int YS = 2 * BN + 16;  // LDS row stride in bytes, padded against bank conflicts
+      static_assert(BM * YS <= NS * C::STAGE, "the tile image must fit in the LDS ring");
+      lds_barrier();  // every wave's DMA has landed (vmcnt(0) above) and its ring reads are done
+      const bool odd = lr & 1;
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+          const int cb = wn * C::WTN + 32 * j + lr - (odd ? 1 : 0);
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float a0 = acc[i][j][r], a1 = acc[i][j][r + 1];  // rows rr and rr + 1, this lane's column
+            // swap with the neighbouring lane (DPP quad permutation 1,0,3,2)
+            const float y = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, odd ? a0 : a1), 0xB1, 0xF, 0xF, false));
+            const int rr = wm * C::WTM + 32 * i + 4 * h + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
+            const v2f pair = {odd ? y : a0, odd ? a1 : y};
+            *(__attribute__((address_space(3))) v2bf*)(smem + rr * YS + 2 * cb) = __builtin_convertvector(pair, v2bf);
+          }
+        }
+      }
+      lds_barrier();
+      constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+      constexpr int NT = C::NW * 64;
+#pragma unroll
+      for (int q0 = 0; q0 < BM * CPR; q0 += NT) {
+        const int q = q0 + tid;
+        const int row = q / CPR, cc = q % CPR;
+        if (q < BM * CPR && m0 + row < S && n0 + 8 * cc < N) {
+          const v4i v = lds4(smem + row * YS + 16 * cc);
+          // streaming store: Y is not read again by this kernel
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(static_cast<__bf16*>(Y) + (long)(m0 + row) * N + n0 + 8 * cc));
+        }
+      }
+      return;
+    }
+  }
+  // fp32 output, or bf16 rows that are not 16-byte aligned: direct 2- / 4-byte stores
   auto store = [&](bool guard) {
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {

@@ -3,10 +3,12 @@
 // quantize) and the offline weight preparation of §3.3 (same kernel, the indexed channel is
 // copied into the contiguous W_L block without zeroing).
 //
-// Data flow: HBM-bound.  Each lane owns one 16-byte chunk (8 bf16) of a row, so a wavefront
-// reads 1 KiB of consecutive memory and G/8 adjacent lanes form one group.  Outputs go to the
-// tiled layout the GEMM streams: codes in panels of 128 channels (R rows x 64 or 128 bytes),
-// scales in panels of 4 groups (8 when G = 16), B / W_L in panels of 32 groups.  The group amax is
+// Data flow: HBM-bound.  Outputs go to the tiled layout the GEMM streams: codes in panels of
+// 128 channels (R rows x 64 or 128 bytes), scales in panels of 4 groups (8 when G = 16), B / W_L
+// in panels of 32 groups.  A wavefront owns 16 rows x one 128-channel panel: per load
+// instruction, 16 lanes cover one row's 256 bytes of the panel (G/8 adjacent lanes form a
+// group) and 4 rows are covered at once; all four loads are issued before any is processed.
+// Its code output is then one contiguous 1 KiB (2 KiB for E4M3) block of the panel.  The group amax is
 // an integer max over the bf16 magnitude bits (|x| ordering == bit ordering for finite values),
 // reduced across the group's lanes with cross-lane swizzles.  The E8M0 code is read straight
 // off the amax exponent field: floor(log2 amax) - emax + 127 = E - 2 (E2M1) or E - 8 (E4M3),
@@ -29,26 +31,18 @@ __device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us
 __device__ __forceinline__ uint32_t as_u32(us2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
 
+// One 16-byte chunk c (8 bf16 of one row): extraction, group scale, encoding, tiled stores.
 template <int G, int FMT, int MODE>
-__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nchunks, int rows, int H, TableArg tab,
-                                               uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
-                                               uint16_t* __restrict__ side) {
+__device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, const TableArg& tab,
+                                            uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
+                                            uint16_t* __restrict__ side) {
   constexpr int LPG = G / 8;  // lanes per group
-  const long c = (long)blockIdx.x * 256 + threadIdx.x;
-  // nchunks is a multiple of LPG and groups start at multiples of LPG, so a group's lanes
-  // are either all in range or all out of range; the cross-lane reductions stay inside a group.
-  if (c >= nchunks) return;
-  const int cpr = H >> 3;
-  const long r = c / cpr;
-  const int col0 = (int)(c - r * cpr) << 3;
   const int k = col0 / G;
   const int q = (col0 % G) >> 3;
   constexpr int SPG = G == 16 ? 8 : 4;  // groups per scale panel
   const long code_at = ((long)(col0 >> 7) * rows + r) * 16 + ((col0 & 127) >> 3);  // in 4 / 8-byte units
   const long scale_at = ((long)(k / SPG) * rows + r) * SPG + k % SPG;
   const long side_at = ((long)(k >> 5) * rows + r) * 32 + (k & 31);
-
-  const u4 v = __builtin_nontemporal_load(X + c);
   uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
 
   if (MODE != kNoTable) {
@@ -110,29 +104,59 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, long nc
   }
 }
 
+constexpr int kRowsPerWave = 16;
+
+template <int G, int FMT, int MODE>
+__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int rows, int H, TableArg tab,
+                                               uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
+                                               uint16_t* __restrict__ side) {
+  const int npan = H >> 7;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave -> (row block, panel), panel fastest
+  const int rb = w / npan;
+  const int p = w - rb * npan;
+  if (rb * kRowsPerWave >= rows) return;  // whole wavefront past the last row
+  const int lane = threadIdx.x & 63;
+  const int cc = lane & 15;  // chunk of the panel row
+  const int col0 = p * 128 + cc * 8;
+  const int r0 = rb * kRowsPerWave + (lane >> 4);
+  // rows past the end are skipped by whole 16-lane row segments, so a group's lanes agree
+  u4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = r0 + 4 * u;
+    if (r < rows) v[u] = __builtin_nontemporal_load(X + (long)r * (H >> 3) + (col0 >> 3));
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = r0 + 4 * u;
+    if (r < rows) quant_chunk<G, FMT, MODE>(v[u], r, col0, rows, tab, Q, SC, side);
+  }
+}
+
 template <int G, int FMT>
-hipError_t dispatch_mode(const void* X, long nchunks, int rows, int H, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+hipError_t dispatch_mode(const void* X, int rows, int H, const TableArg* tab, int mode, void* Q, uint8_t* SC,
                          void* side, hipStream_t st) {
-  const unsigned grid = (unsigned)((nchunks + 255) / 256);
+  const long waves = (long)((rows + kRowsPerWave - 1) / kRowsPerWave) * (H >> 7);
+  const unsigned grid = (unsigned)((waves + 3) / 4);
   const u4* x = static_cast<const u4*>(X);
   uint8_t* q = static_cast<uint8_t*>(Q);
   uint16_t* sd = static_cast<uint16_t*>(side);
   static const TableArg empty = {};
   const TableArg& t = tab ? *tab : empty;
   if (mode == kExtractZero)
-    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, nchunks, rows, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   else if (mode == kCopyOnly)
-    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, nchunks, rows, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   else
-    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, nchunks, rows, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t dispatch_fmt(const void* X, long nchunks, int rows, int H, const TableArg* tab, int mode, osc_fmt fmt,
+hipError_t dispatch_fmt(const void* X, int rows, int H, const TableArg* tab, int mode, osc_fmt fmt,
                         void* Q, uint8_t* SC, void* side, hipStream_t st) {
-  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, nchunks, rows, H, tab, mode, Q, SC, side, st);
-  return dispatch_mode<G, OSC_MXFP8>(X, nchunks, rows, H, tab, mode, Q, SC, side, st);
+  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, rows, H, tab, mode, Q, SC, side, st);
+  return dispatch_mode<G, OSC_MXFP8>(X, rows, H, tab, mode, Q, SC, side, st);
 }
 
 // ------------------------------------------------------------------ table builder
@@ -189,9 +213,9 @@ hipError_t launch_quant(const void* X, int rows, int H, int G, const TableArg* t
   const long nchunks = (long)rows * (H / 8);
   if (nchunks == 0) return hipSuccess;
   switch (G) {
-    case 16: return dispatch_fmt<16>(X, nchunks, rows, H, tab, mode, fmt, Q, SC, side, st);
-    case 32: return dispatch_fmt<32>(X, nchunks, rows, H, tab, mode, fmt, Q, SC, side, st);
-    default: return dispatch_fmt<64>(X, nchunks, rows, H, tab, mode, fmt, Q, SC, side, st);
+    case 16: return dispatch_fmt<16>(X, rows, H, tab, mode, fmt, Q, SC, side, st);
+    case 32: return dispatch_fmt<32>(X, rows, H, tab, mode, fmt, Q, SC, side, st);
+    default: return dispatch_fmt<64>(X, rows, H, tab, mode, fmt, Q, SC, side, st);
   }
 }
 
