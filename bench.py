@@ -21,6 +21,7 @@ Prints ONE JSON line.  Extra per-workload rows (FFN prefill / decode, W2 FP8 fal
 group-size sweep) go under "rows".
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -149,6 +150,8 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
             quant(l)
             gemm(l)
         ev = TimingEvents(2 * steps + 1)
+        gc.collect()
+        gc.disable()  # no collector pause inside the timed region
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
@@ -160,6 +163,7 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
         ev.record(2 * steps, s)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        gc.enable()
     tq = sum(ev.ms(2 * i, 2 * i + 1) for i in range(steps)) / steps * 1e-3
     tg = sum(ev.ms(2 * i + 1, 2 * i + 2) for i in range(steps)) / steps * 1e-3
     ev.close()

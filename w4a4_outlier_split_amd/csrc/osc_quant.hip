@@ -69,11 +69,11 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, con
   m = __builtin_elementwise_max(m, as_us2(w2 & 0x7FFF7FFFu));
   m = __builtin_elementwise_max(m, as_us2(w3 & 0x7FFF7FFFu));
   int amax = m.x > m.y ? m.x : m.y;
-#pragma unroll
-  for (int off = 1; off < LPG; off <<= 1) {
-    const int o = __shfl_xor(amax, off, 64);
-    amax = o > amax ? o : amax;
-  }
+  // group max across the LPG adjacent lanes with DPP lane swaps: neighbours (quad_perm 1,0,3,2),
+  // pairs (quad_perm 2,3,0,1), then the two quads of an 8-lane row half (half-row mirror)
+  amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0xB1, 0xF, 0xF, false));
+  if constexpr (LPG >= 4) amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0x4E, 0xF, 0xF, false));
+  if constexpr (LPG >= 8) amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0x141, 0xF, 0xF, false));
   const int E = amax >> 7;
   const int sx = FMT == OSC_MXFP4 ? (E > 2 ? E - 2 : 0) : (E > 8 ? E - 8 : 0);
   if (q == 0) SC[scale_at] = (uint8_t)sx;
