@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the extra workload rows")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--only", default=None, help="time only this workload row (profiling runs)")
+    p.add_argument("--quality", action="store_true",
+                   help="also report the relative error of each path against the exact product (sampled rows)")
     p.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                    help="also run one plain device copy of MB MiB (calibrates HBM traffic counters)")
     return p.parse_args()
@@ -229,6 +231,42 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup):
     return row
 
 
+def quality(torch, osc, w, variants, dev, nrows=32, seed=7):
+    """Relative error ||Y - X W^T|| / ||X W^T|| on sampled token rows (all N outputs), against the
+    exact product of the bf16 inputs (fp64 on the host), for each (name, L, afmt, wfmt) variant.
+    A synthetic stand-in for the pages' accuracy comparison: context, not a gate."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(w.S, size=min(nrows, w.S), replace=False))
+    xf = (w.X[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wf = (w.W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = xf @ wf.T
+    nref = float(np.linalg.norm(ref))
+    Xd = torch.from_numpy(w.X.view(np.int16)).to(dev)
+    Wd = torch.from_numpy(w.W.view(np.int16)).to(dev)
+    S, H, N, G = w.S, w.H, w.N, w.G
+    u8 = lambda n: torch.empty((n,), dtype=torch.uint8, device=dev)
+    side = lambda R: torch.empty((osc.side_elems(R, H, G),), dtype=torch.int16, device=dev)
+    out = {}
+    for name, L, afmt, wfmt in variants:
+        QX, SX, B = u8(osc.code_bytes(S, H, afmt)), u8(osc.scale_bytes(S, H, G)), side(S) if L is not None else None
+        QW, SW, WL = u8(osc.code_bytes(N, H, wfmt)), u8(osc.scale_bytes(N, H, G)), side(N) if L is not None else None
+        Y = torch.empty((S, N), dtype=torch.float32, device=dev)
+        osc.osc_pack_weights(Wd, N, H, G, L, wfmt, QW, SW, WL)
+        osc.osc_quant_act(Xd, S, H, G, L, afmt, QX, SX, B)
+        if afmt == osc.OSC_MXFP4:
+            osc.osc_gemm(QX, SX, B, QW, SW, WL, S, N, H, G, Y, osc.OSC_Y_F32)
+        else:
+            osc.osc_gemm_fp8(QX, SX, QW, SW, wfmt, S, N, H, G, Y, osc.OSC_Y_F32)
+        torch.cuda.synchronize()
+        got = Y[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+        out[name] = float(np.linalg.norm(got - ref)) / nref
+        del QX, SX, B, QW, SW, WL, Y
+    del Xd, Wd
+    torch.cuda.empty_cache()
+    return {"metric": "||Y - X W^T|| / ||X W^T||", "rows_sampled": int(len(rows)), "errors": out}
+
+
 def cpu_baseline(w, L, target_s):
     """The oracle (quant + dual-path GEMM, fp64) on the first rows of the same workload,
     grown until the sample costs about target_s seconds of CPU time."""
@@ -286,6 +324,17 @@ def main():
         head = run_row(torch, osc, "qkv_proj_s2048_g32", w, L, osc.OSC_MXFP4, osc.OSC_MXFP4, dev, stream,
                        args.steps, args.warmup)
 
+    # ---- the W8A8 comparator of the pages' speedup table, same shape: MXFP8 activations and
+    # weights, no extraction
+    comparator = None
+    if args.only in (None, "qkv", "w8a8"):
+        r8 = run_row(torch, osc, "qkv_proj_s2048_w8a8", w, None, osc.OSC_MXFP8, osc.OSC_MXFP8, dev, stream,
+                     max(20, args.steps // 2), args.warmup)
+        rows.append(r8)
+        if head is not None:
+            comparator = {"w8a8_ms_per_step": r8["ms_per_step"], "osc_ms_per_step": head["ms_per_step"],
+                          "osc_speedup_vs_w8a8": r8["ms_per_step"] / head["ms_per_step"]}
+
     # ---- more rows of the same path at the other configurations
     if not args.no_rows:
         def want(n):
@@ -294,7 +343,10 @@ def main():
             wf = synth.ffn_up(S=4096)
             Lf = table_on_gpu(torch, osc, wf, 32, dev)
             if want("ffn_up_s4096"):
-                rows.append(run_row(torch, osc, "ffn_up_s4096_g32", wf, Lf, 0, 0, dev, stream, 50, 10))
+                ru = run_row(torch, osc, "ffn_up_s4096_g32", wf, Lf, 0, 0, dev, stream, 50, 10)
+                r8 = run_row(torch, osc, "ffn_up_s4096_w8a8", wf, None, 1, 1, dev, stream, 50, 10)
+                r8["osc_speedup_vs_w8a8"] = r8["ms_per_step"] / ru["ms_per_step"]
+                rows += [ru, r8]
             if want("ffn_up_s16"):
                 wd = synth.ffn_up(S=16)
                 r = run_row(torch, osc, "ffn_up_s16_g32_decode", wd, Lf, 0, 0, dev, stream, 200, 20)
@@ -321,8 +373,19 @@ def main():
                     r["gemm_frac_of_hbm"] = r["gemm_gbs"] / PEAK_HBM_GBS
                 rows.append(r)
 
+    # ---- quality side-measure (sampled rows, exact fp64 reference on the host)
+    qual = None
+    if args.quality:
+        qual = {"qkv_s2048": quality(torch, osc, w, [("osc", L, 0, 0), ("mxfp4_direct", None, 0, 0),
+                                                      ("w8a4_fp8", None, 1, 0), ("w8a8", None, 1, 1)], dev)}
+        wdn = synth.ffn_down(S=4096)
+        Ld = table_on_gpu(torch, osc, wdn, 32, dev)
+        qual["ffn_down_s4096"] = quality(torch, osc, wdn, [("w8a4_fp8", None, 1, 0), ("forced_osc", Ld, 0, 0),
+                                                           ("mxfp4_direct", None, 0, 0)], dev, nrows=16)
+        del wdn
+
     if head is None:
-        print(json.dumps({"rows": rows}))
+        print(json.dumps({"rows": rows, "quality": qual}))
         return
 
     # ---- roofline of the dominant kernel (the GEMM, MFMA-bound)
@@ -360,6 +423,8 @@ def main():
         "quant_roofline": {"bound": "hbm", "achieved": head["quant_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": head["quant_gbs"] / PEAK_HBM_GBS},
         "cpu_baseline": cpu,
+        "comparator": comparator,
+        "quality": qual,
         "rows": rows,
         "bench_seconds": time.perf_counter() - t_start,
     }
