@@ -327,7 +327,7 @@ def main():
     # ---- the W8A8 comparator of the pages' speedup table, same shape: MXFP8 activations and
     # weights, no extraction
     comparator = None
-    if args.only in (None, "qkv", "w8a8"):
+    if args.only in (None, "w8a8"):
         r8 = run_row(torch, osc, "qkv_proj_s2048_w8a8", w, None, osc.OSC_MXFP8, osc.OSC_MXFP8, dev, stream,
                      max(20, args.steps // 2), args.warmup)
         rows.append(r8)
