@@ -51,6 +51,14 @@ def lib():
         L.orc_gemm.restype = None
         L.orc_build_table.argtypes = [P, i, i, i, ctypes.c_double, ctypes.c_double, P, P, P]
         L.orc_build_table.restype = i
+        L.orc_gemm_comp.argtypes = [P, P, i, P, P, P, i, P, i, i, i, i, i, P]
+        L.orc_gemm_comp.restype = None
+        L.orc_quant_act_multi.argtypes = [P, i, i, i, P, i, i, P, P, P]
+        L.orc_quant_act_multi.restype = None
+        L.orc_pack_weights_multi.argtypes = [P, i, i, i, P, i, i, P, P, P]
+        L.orc_pack_weights_multi.restype = None
+        L.orc_build_table_multi.argtypes = [P, i, i, i, ctypes.c_double, ctypes.c_double, i, P, P, P]
+        L.orc_build_table_multi.restype = i
         L.orc_threads.argtypes = []
         L.orc_threads.restype = i
         _lib = L
@@ -164,3 +172,63 @@ def osc_linear(X, W, G: int, L, fmt: int = MXFP4):
     QX, SX, B = quant_act(X, G, L, fmt)
     QW, SW, WL = pack_weights(W, G, L, MXFP4 if fmt == MXFP8 else fmt)
     return gemm(QX, SX, QW, SW, G, B, WL, afmt=fmt, wfmt=MXFP4 if fmt == MXFP8 else fmt)
+
+
+# ------------------------------------------------ several channels per group (§6)
+
+def quant_act_multi(X: np.ndarray, G: int, L: np.ndarray, m: int, fmt: int = MXFP4):
+    """L: int32[K, m] (or K*m flat) -> (QX, SX uint8[S, K], B uint16[S, K*m])."""
+    X = _c(X, np.uint16)
+    S, H = X.shape
+    K = H // G
+    Lc = _c(L, np.int32).reshape(K * m)
+    QX = np.zeros((S, code_bytes_per_row(H, fmt)), np.uint8)
+    SX = np.zeros((S, K), np.uint8)
+    B = np.zeros((S, K * m), np.uint16)
+    lib().orc_quant_act_multi(_p(X), S, H, G, _p(Lc), m, fmt, _p(QX), _p(SX), _p(B))
+    return QX, SX, B
+
+
+def pack_weights_multi(W: np.ndarray, G: int, L: np.ndarray, m: int, fmt: int = MXFP4):
+    """-> (QW, SW uint8[N, K], WL uint16[N, K*m])."""
+    W = _c(W, np.uint16)
+    N, H = W.shape
+    K = H // G
+    Lc = _c(L, np.int32).reshape(K * m)
+    QW = np.zeros((N, code_bytes_per_row(H, fmt)), np.uint8)
+    SW = np.zeros((N, K), np.uint8)
+    WL = np.zeros((N, K * m), np.uint16)
+    lib().orc_pack_weights_multi(_p(W), N, H, G, _p(Lc), m, fmt, _p(QW), _p(SW), _p(WL))
+    return QW, SW, WL
+
+
+def gemm_comp(QX, SX, QW, SW, G: int, B, WL, afmt: int = MXFP4, wfmt: int = MXFP4) -> np.ndarray:
+    """Dual-path GEMM with B / WL of any number of compensation columns (S x KC, N x KC)."""
+    QX, SX, QW, SW = _c(QX, np.uint8), _c(SX, np.uint8), _c(QW, np.uint8), _c(SW, np.uint8)
+    Bc, WLc = _c(B, np.uint16), _c(WL, np.uint16)
+    S, N = QX.shape[0], QW.shape[0]
+    H = SX.shape[1] * G
+    KC = Bc.shape[1]
+    assert WLc.shape == (N, KC)
+    Y = np.zeros((S, N), np.float64)
+    lib().orc_gemm_comp(_p(QX), _p(SX), afmt, _p(Bc), _p(QW), _p(SW), wfmt, _p(WLc), S, N, H, G, KC, _p(Y))
+    return Y
+
+
+def build_table_multi(Xcal: np.ndarray, G: int, m: int, alpha: float = 5.0, rho: float = 0.35):
+    """-> (L int32[K, m], hits int32[K, m], events int32[K])."""
+    Xcal = _c(Xcal, np.uint16)
+    R, H = Xcal.shape
+    K = H // G
+    L = np.zeros((K, m), np.int32)
+    hits = np.zeros((K, m), np.int32)
+    events = np.zeros(K, np.int32)
+    lib().orc_build_table_multi(_p(Xcal), R, H, G, float(alpha), float(rho), m, _p(L), _p(hits), _p(events))
+    return L, hits, events
+
+
+def osc_linear_multi(X, W, G: int, L, m: int):
+    """The whole layer with m protected channels per group, in fp64."""
+    QX, SX, B = quant_act_multi(X, G, L, m)
+    QW, SW, WL = pack_weights_multi(W, G, L, m)
+    return gemm_comp(QX, SX, QW, SW, G, B, WL)

@@ -31,6 +31,14 @@
  *   - W_L is stored output-major: WL[n*K + k] = W[n, k*G + L[k]] (0 if L[k] = -1),
  *     i.e. the K x N slice of the page kept in the same out x in layout as W;
  *   - the FP8 fallback extracts nothing (no B, no W_L).
+ *
+ * §6 names, as a direction only, protecting 2-3 channels per group in extreme
+ * cases.  The *_multi functions read it plainly: the table holds m entries per
+ * group (distinct offsets, or -1), every listed channel is copied into its own
+ * column of B (S x mK, column k*m + j for entry j of group k) and zeroed, the
+ * scale is computed on the group with all of them zeroed, W_L has the same mK
+ * columns, and the compensation is B·W_L over mK.  With m = 1 they are the
+ * single-channel functions above.
  */
 #include <math.h>
 #include <omp.h>
@@ -199,9 +207,9 @@ void orc_pack_weights(const uint16_t* W, int N, int H, int G, const int32_t* L, 
  * in fp64 (every product of two decoded codes, and of two bf16 values, is
  * exact in fp64).  B / WL may be NULL: no compensation path (plain MX GEMM,
  * and the FP8 fallback of §4).  afmt / wfmt: element format of each side. */
-void orc_gemm(const uint8_t* QX, const uint8_t* SX, int afmt, const uint16_t* B,
-              const uint8_t* QW, const uint8_t* SW, int wfmt, const uint16_t* WL,
-              int S, int N, int H, int G, double* Y) {
+void orc_gemm_comp(const uint8_t* QX, const uint8_t* SX, int afmt, const uint16_t* B,
+                   const uint8_t* QW, const uint8_t* SW, int wfmt, const uint16_t* WL,
+                   int S, int N, int H, int G, int KC, double* Y) {
   int K = H / G;
   long xstride = (afmt == ORC_MXFP4) ? H / 2 : H;
   long wstride = (wfmt == ORC_MXFP4) ? H / 2 : H;
@@ -217,11 +225,59 @@ void orc_gemm(const uint8_t* QX, const uint8_t* SX, int afmt, const uint16_t* B,
         y += ldexp(part, ((int)SX[(long)s * K + k] - 127) + ((int)SW[(long)n * K + k] - 127));
       }
       if (B && WL)
-        for (int k = 0; k < K; ++k)
-          y += orc_bf16_value(B[(long)s * K + k]) * orc_bf16_value(WL[(long)n * K + k]);
+        for (int c = 0; c < KC; ++c)
+          y += orc_bf16_value(B[(long)s * KC + c]) * orc_bf16_value(WL[(long)n * KC + c]);
       Y[(long)s * N + n] = y;
     }
   }
+}
+
+/* The single-channel product: KC = K compensation columns. */
+void orc_gemm(const uint8_t* QX, const uint8_t* SX, int afmt, const uint16_t* B,
+              const uint8_t* QW, const uint8_t* SW, int wfmt, const uint16_t* WL,
+              int S, int N, int H, int G, double* Y) {
+  orc_gemm_comp(QX, SX, afmt, B, QW, SW, wfmt, WL, S, N, H, G, H / G, Y);
+}
+
+/* ------------------------------------------------- several channels (§6) */
+
+/* Activations with m protected channels per group: entry j of group k is
+ * L[k*m + j] (an offset in [0, G), or -1).  Every listed channel is copied into
+ * B[s, k*m + j] (0 for -1) and zeroed; the group is then quantized as in §3.2.
+ * B: S x (K*m) bf16 bits. */
+void orc_quant_act_multi(const uint16_t* X, int S, int H, int G, const int32_t* L, int m, int fmt,
+                         uint8_t* QX, uint8_t* SX, uint16_t* B) {
+  int K = H / G;
+  long qstride = (fmt == ORC_MXFP4) ? H / 2 : H;
+#pragma omp parallel for schedule(static)
+  for (int s = 0; s < S; ++s) {
+    double vals[256];
+    for (int k = 0; k < K; ++k) {
+      for (int j = 0; j < G; ++j) vals[j] = orc_bf16_value(X[(long)s * H + k * G + j]);
+      for (int e = 0; e < m; ++e) {
+        int c = L[k * m + e];
+        B[(long)s * K * m + k * m + e] = (c >= 0) ? X[(long)s * H + k * G + c] : 0;
+      }
+      for (int e = 0; e < m; ++e)
+        if (L[k * m + e] >= 0) vals[L[k * m + e]] = 0.0;
+      quant_group(vals, G, fmt, QX + s * qstride, k * G, SX + (long)s * K + k);
+    }
+  }
+}
+
+/* Weights with m protected channels per group: W quantized unmodified,
+ * WL[n, k*m + j] = W[n, kG + L[k*m + j]] (0 for -1).  WL: N x (K*m). */
+void orc_pack_weights_multi(const uint16_t* W, int N, int H, int G, const int32_t* L, int m, int fmt,
+                            uint8_t* QW, uint8_t* SW, uint16_t* WL) {
+  int K = H / G;
+  orc_pack_weights(W, N, H, G, NULL, fmt, QW, SW, NULL);
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int k = 0; k < K; ++k)
+      for (int e = 0; e < m; ++e) {
+        int c = L[k * m + e];
+        WL[(long)n * K * m + k * m + e] = (c >= 0) ? W[(long)n * H + k * G + c] : 0;
+      }
 }
 
 /* ------------------------------------------------------- table builder */
@@ -277,4 +333,65 @@ int orc_build_table(const uint16_t* Xcal, int R, int H, int G, double alpha, dou
     }
   }
   return protected_groups;
+}
+
+/* Table slice with up to m channels per group (§6 direction, read as above):
+ * in every calibration row, each of the m largest |x| of the group (lower
+ * channel first among equal magnitudes) that exceeds alpha times the group's
+ * mean |x| is an event of its channel; a row with at least one event counts in
+ * events[k].  Channels are ranked by event count (lower channel first on ties)
+ * and entry j is the j-th ranked channel if its count reaches rho * R, else -1
+ * (and so are the entries after it).  hits[k*m + j] = the j-th ranked
+ * channel's count, kept or not.  With m = 1 this is orc_build_table.  Returns
+ * the entries kept. */
+int orc_build_table_multi(const uint16_t* Xcal, int R, int H, int G, double alpha, double rho, int m,
+                          int32_t* L, int32_t* hits, int32_t* events) {
+  int K = H / G;
+  int kept = 0;
+  for (int k = 0; k < K; ++k) {
+    long hist[256];
+    for (int j = 0; j < G; ++j) hist[j] = 0;
+    long nev = 0;
+    for (int r = 0; r < R; ++r) {
+      double a[256], sum = 0.0;
+      int used[256];
+      for (int j = 0; j < G; ++j) {
+        a[j] = fabs(orc_bf16_value(Xcal[(long)r * H + k * G + j]));
+        sum += a[j];
+        used[j] = 0;
+      }
+      double mean = sum / G;
+      int any = 0;
+      for (int e = 0; e < m; ++e) {
+        int jr = -1;
+        for (int j = 0; j < G; ++j)
+          if (!used[j] && (jr < 0 || a[j] > a[jr])) jr = j;
+        used[jr] = 1;
+        if (a[jr] > alpha * mean) {
+          hist[jr] += 1;
+          any = 1;
+        }
+      }
+      nev += any;
+    }
+    events[k] = (int32_t)nev;
+    int taken[256];
+    for (int j = 0; j < G; ++j) taken[j] = 0;
+    int stop = 0;
+    for (int e = 0; e < m; ++e) {
+      int js = -1;
+      for (int j = 0; j < G; ++j)
+        if (!taken[j] && (js < 0 || hist[j] > hist[js])) js = j;
+      taken[js] = 1;
+      hits[k * m + e] = (int32_t)hist[js];
+      if (!stop && hist[js] > 0 && (double)hist[js] >= rho * (double)R) {
+        L[k * m + e] = js;
+        ++kept;
+      } else {
+        stop = 1;
+        L[k * m + e] = -1;
+      }
+    }
+  }
+  return kept;
 }

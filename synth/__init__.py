@@ -188,3 +188,45 @@ def random_bf16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     """Plain N(0, scale^2) bf16 bits, for small edge-case tests."""
     z = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(scale)
     return to_bf16_bits(z)
+
+
+def draw_plant_pairs(seed: int, H: int, frac_pair: float, frac_single: float, lo: float, hi: float) -> Plant:
+    """Plant two persistent channels in round(frac_pair*K32) blocks and one in
+    round(frac_single*K32) other blocks; offsets inside a pair are distinct."""
+    rng = np.random.default_rng(seed)
+    nblk = H // PLANT_BLOCK
+    n2, n1 = int(round(frac_pair * nblk)), int(round(frac_single * nblk))
+    blocks = rng.choice(nblk, n2 + n1, replace=False)
+    groups, offsets, factors = [], [], []
+    for i, b in enumerate(blocks):
+        offs = rng.choice(PLANT_BLOCK, 2 if i < n2 else 1, replace=False)
+        for o in offs:
+            groups.append(b)
+            offsets.append(o)
+            factors.append(rng.uniform(lo, hi))
+    return Plant(np.array(groups, np.int64), np.array(offsets, np.int64), np.array(factors))
+
+
+def planted_table_multi(plant: Plant, H: int, G: int, m: int) -> np.ndarray:
+    """The planted channels as an m-entry table slice (offsets ascending, -1 padded)."""
+    K = H // G
+    L = np.full((K, m), -1, dtype=np.int32)
+    per = {}
+    for c in plant.channels.tolist():
+        per.setdefault(c // G, []).append(c % G)
+    for k, offs in per.items():
+        offs = sorted(offs)[:m]
+        L[k, :len(offs)] = offs
+    return L
+
+
+def two_outlier_groups(S: int = 2048) -> Workload:
+    """QKV shape (H=4096, N=6144, G=32) where 40% of the groups carry two persistent channels
+    (x U(40,100) each) and 30% carry one; 0.1% x20 spikes.  L = the planted channels, 2 per group
+    (the page's §6 case for protecting more than one channel)."""
+    H, N, G = 4096, 6144, 32
+    plant = draw_plant_pairs(51, H, 0.40, 0.30, 40.0, 100.0)
+    X = draw_x_bernoulli_spikes(S, H, plant, 52, 53)
+    calib = draw_x_bernoulli_spikes(CALIB_ROWS, H, plant, 54, 54 + 100)
+    return Workload(f"two_outlier_s{S}", S, H, N, G, X, 55, calib, planted_table_multi(plant, H, G, 2), plant)
+

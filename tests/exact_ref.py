@@ -88,8 +88,15 @@ def decode(code: int, fp8: bool) -> F:
     return -mag if code & 8 else mag
 
 
-def quant_rows(rows: List[List[int]], G: int, L: Optional[List[int]], fp8: bool):
-    """rows: bf16 bit patterns.  Returns (codes[s][h], exps[s][k], B[s][k] bf16 bits)."""
+def _channels(entry) -> List[int]:
+    """A table entry: one offset (the page's single channel) or a sequence of them (§6)."""
+    return list(entry) if isinstance(entry, (list, tuple)) else [entry]
+
+
+def quant_rows(rows: List[List[int]], G: int, L: Optional[List], fp8: bool):
+    """rows: bf16 bit patterns.  Returns (codes[s][h], exps[s][k], B[s][c] bf16 bits).
+    L[k] is an offset (-1 = none) or a list of m of them; B then has one column per listed
+    entry, group-major (column k*m + j)."""
     codes_all, exps_all, b_all = [], [], []
     for row in rows:
         H = len(row)
@@ -98,16 +105,17 @@ def quant_rows(rows: List[List[int]], G: int, L: Optional[List[int]], fp8: bool)
             bits = list(row[k * G:(k + 1) * G])
             vals = [bf16(b) for b in bits]
             neg = [is_negative(b) for b in bits]
-            bval = 0
-            if L is not None and L[k] >= 0:
-                c = L[k]
-                bval = bits[c]
-                vals[c] = F(0)
-                neg[c] = False
+            if L is not None:
+                chans = _channels(L[k])
+                for c in chans:
+                    b_row.append(bits[c] if c >= 0 else 0)
+                for c in chans:
+                    if c >= 0:
+                        vals[c] = F(0)
+                        neg[c] = False
             e, codes = quant_group(vals, neg, fp8)
             codes_row += codes
             exps_row.append(e)
-            b_row.append(bval)
         codes_all.append(codes_row)
         exps_all.append(exps_row)
         b_all.append(b_row)
@@ -132,9 +140,12 @@ def osc_linear(X: List[List[int]], W: List[List[int]], G: int, L: Optional[List[
                 part = sum(decode(qx[s][k * G + j], act_fp8) * decode(qw[n][k * G + j], w_fp8) for j in range(G))
                 y += part * F(2) ** (ex[s][k] + ew[n][k])
             if Lx is not None:
+                col = 0
                 for k in range(K):
-                    if L[k] >= 0:
-                        y += bf16(bx[s][k]) * bf16(W[n][k * G + L[k]])
+                    for c in _channels(L[k]):
+                        if c >= 0:
+                            y += bf16(bx[s][col]) * bf16(W[n][k * G + c])
+                        col += 1
             out.append(y)
         Y.append(out)
     return Y
