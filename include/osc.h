@@ -81,6 +81,7 @@ typedef enum {
 } osc_ytype;
 
 #define OSC_MAX_GROUPS 1024
+#define OSC_MAX_CHANNELS 3 /* protected channels per group in the *_multi calls */
 
 /*
  * osc_pack_weights -- offline weight preparation (§3.2 weight side, §3.3).
@@ -156,6 +157,42 @@ osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, cons
  */
 osc_status osc_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho,
                            int32_t* L, int32_t* hits, int32_t* events, void* stream);
+
+/*
+ * Several protected channels per group.  The page's outlook (§6) names, as a
+ * direction for extreme cases, protecting 2-3 channels per group instead of
+ * one; it does not define the method further.  These calls read it plainly:
+ *   - the table slice L holds m entries per group, entry e of group k at
+ *     L[k*m + e]: distinct offsets in [0, G), or -1 (OSC_E_TABLE otherwise);
+ *   - every listed channel is copied into its own compensation column
+ *     c = k*m + e of B / W_L and (activations) zeroed before the group scale is
+ *     computed; a -1 entry gives a +0 column;
+ *   - Y = (Q_X ⊗ Q_W)·S + sum over the m*K columns of B(s,c)·WL(n,c).
+ * B and W_L use the tiled layout above with m*K columns instead of K
+ * (ceil(m*K/32)*32*R bf16 elements).  m = 1 is exactly the single-channel
+ * call of the same name without the suffix.  Constraints as for those calls,
+ * plus 1 <= m <= OSC_MAX_CHANNELS, m*K <= OSC_MAX_GROUPS, and for the GEMM with
+ * compensation (m*K) % 8 == 0.
+ */
+osc_status osc_quant_act_multi(const void* X, int S, int H, int G, const int32_t* L, int m, osc_fmt afmt,
+                               void* QX, uint8_t* SX, void* B, void* stream);
+osc_status osc_pack_weights_multi(const void* W, int N, int H, int G, const int32_t* L, int m, osc_fmt wfmt,
+                                  void* QW, uint8_t* SW, void* WL, void* stream);
+osc_status osc_gemm_multi(const void* QX, const uint8_t* SX, const void* B, const void* QW,
+                          const uint8_t* SW, const void* WL, int S, int N, int H, int G, int m, void* Y,
+                          osc_ytype yt, void* stream);
+/*
+ * Table slice with up to m entries per group.  Reading: in every calibration
+ * row, each of the group's m largest |x| (lower channel first among equal
+ * magnitudes) that exceeds alpha times the group's mean |x| is an event of its
+ * channel; entry e is the e-th most frequent event channel (lower channel
+ * first on ties) while its count reaches rho * R, then -1.  With m = 1 this is
+ * osc_build_table.  L, hits: device int32[K*m] (hits: the e-th ranked
+ * channel's count, kept or not); events: device int32[K], rows with at least
+ * one event.
+ */
+osc_status osc_build_table_multi(const void* Xcal, int R, int H, int G, double alpha, double rho, int m,
+                                 int32_t* L, int32_t* hits, int32_t* events, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* osc_status_str(osc_status s);

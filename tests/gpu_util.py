@@ -40,10 +40,10 @@ def code_cols(H: int, fmt: int) -> int:
     return H // 2 if fmt == osc.OSC_MXFP4 else H
 
 
-def _tiled_outputs(R: int, H: int, G: int, fmt: int, with_side: bool):
+def _tiled_outputs(R: int, H: int, G: int, fmt: int, with_side: bool, m: int = 1):
     Q = poisoned((osc.code_bytes(R, H, fmt),), torch.uint8)
     SC = poisoned((osc.scale_bytes(R, H, G),), torch.uint8)
-    side = poisoned((osc.side_elems(R, H, G),), torch.int16) if with_side else None
+    side = poisoned((osc.side_elems(R, H, G, m),), torch.int16) if with_side else None
     return Q, SC, side
 
 
@@ -61,6 +61,25 @@ def pack(W_dev: torch.Tensor, N: int, H: int, G: int, L, fmt: int):
     return QW, SW, WL
 
 
+def quant_multi(X_dev: torch.Tensor, S: int, H: int, G: int, L, m: int, fmt: int = osc.OSC_MXFP4):
+    """-> tiled device buffers (QX, SX, B with m*K compensation columns)."""
+    QX, SX, B = _tiled_outputs(S, H, G, fmt, True, m)
+    osc.osc_quant_act_multi(X_dev, S, H, G, L, m, fmt, QX, SX, B)
+    return QX, SX, B
+
+
+def pack_multi(W_dev: torch.Tensor, N: int, H: int, G: int, L, m: int, fmt: int = osc.OSC_MXFP4):
+    QW, SW, WL = _tiled_outputs(N, H, G, fmt, True, m)
+    osc.osc_pack_weights_multi(W_dev, N, H, G, L, m, fmt, QW, SW, WL)
+    return QW, SW, WL
+
+
+def gemm_multi(QX, SX, B, QW, SW, WL, S, N, H, G, m, yt=osc.OSC_Y_F32):
+    Y = poisoned((S, N), torch.float32 if yt == osc.OSC_Y_F32 else torch.bfloat16)
+    osc.osc_gemm_multi(QX, SX, B, QW, SW, WL, S, N, H, G, m, Y, yt)
+    return Y
+
+
 def codes_rm(t: torch.Tensor, R: int, H: int, fmt: int) -> np.ndarray:
     """tiled codes -> uint8[R, H/2 or H] row-major (panels of 128 channels)."""
     cb = 64 if fmt == osc.OSC_MXFP4 else 128
@@ -76,12 +95,12 @@ def scales_rm(t: torch.Tensor, R: int, H: int, G: int) -> np.ndarray:
     return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(R, K))
 
 
-def side_rm(t: torch.Tensor, R: int, H: int, G: int) -> np.ndarray:
-    """tiled B / W_L -> uint16 bf16 bits [R, K] row-major (panels of 32 groups)."""
-    K = H // G
-    kp = (K + 31) // 32
+def side_rm(t: torch.Tensor, R: int, H: int, G: int, m: int = 1) -> np.ndarray:
+    """tiled B / W_L -> uint16 bf16 bits [R, m*K] row-major (panels of 32 columns)."""
+    KC = m * (H // G)
+    kp = (KC + 31) // 32
     a = host_bits16(t).reshape(kp, R, 32)
-    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(R, kp * 32)[:, :K])
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(R, kp * 32)[:, :KC])
 
 
 def gemm(QX, SX, B, QW, SW, WL, S, N, H, G, yt=osc.OSC_Y_F32):

@@ -108,3 +108,26 @@ def test_build_table_validation():
     assert b(al=0.0) == 2 and b(rho=0.0) == 2 and b(rho=1.5) == 2
     assert b(L=None) == 1
     assert b(X=U) == 4
+
+
+def test_multi_validation():
+    K = 8  # H=256, G=32
+    good, gp = L8([0, 5] * K)
+    dup, dp = L8([3, 3] + [0, 5] * (K - 1))        # channel listed twice in group 0
+    q = lambda l=gp, m=2, H=256, B=A: status("osc_quant_act_multi", A, 16, H, 32, l, m, 0, A, A, B, None)
+    assert q(m=0) == 2 and q(m=4) == 2           # 1 <= m <= OSC_MAX_CHANNELS
+    assert q(l=dp) == 3                           # duplicate channel in a group
+    bad, bp = L8([0, 32] * K)
+    assert q(l=bp) == 3                           # entry >= G
+    none_ok, np_ = L8([-1, -1] * K)
+    assert q(l=np_, H=384) == 2                   # tiled layout: H % 256
+    p = lambda l=gp, m=2: status("osc_pack_weights_multi", A, 64, 256, 32, l, m, 0, A, A, A, None)
+    assert p(l=dp) == 3 and p(m=5) == 2
+    g = lambda m=2, H=256, G=32, B=A, WL=A: status("osc_gemm_multi", A, A, B, A, A, WL, 16, 64, H, G, m, A, 0, None)
+    assert g(m=0) == 2
+    assert g(H=256, G=64, m=1) == 2               # compensation columns m*K = 4: not a multiple of 8
+    assert g(H=256, G=64, m=3) == 2               # 12 columns
+    assert g(H=65536, G=64, m=2) == 2             # m*K = 2048 > OSC_MAX_GROUPS
+    b = lambda m=2: status("osc_build_table_multi", A, 1536, 256, 32, ctypes.c_double(5.0), ctypes.c_double(0.35),
+                           m, A, A, A, None)
+    assert b(m=0) == 2 and b(m=4) == 2

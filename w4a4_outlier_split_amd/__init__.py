@@ -29,12 +29,14 @@ OSC_MXFP8 = 1
 OSC_Y_BF16 = 0
 OSC_Y_F32 = 1
 OSC_MAX_GROUPS = 1024
+OSC_MAX_CHANNELS = 3
 
 STATUS = {0: "OSC_OK", 1: "OSC_E_NULL", 2: "OSC_E_SHAPE", 3: "OSC_E_TABLE", 4: "OSC_E_ALIGN",
           5: "OSC_E_FORMAT", 6: "OSC_E_DEVICE"}
 
-EXPORTS = ("osc_pack_weights", "osc_quant_act", "osc_gemm", "osc_gemm_fp8", "osc_build_table", "osc_status_str",
-           "osc_last_device_error")
+EXPORTS = ("osc_pack_weights", "osc_quant_act", "osc_gemm", "osc_gemm_fp8", "osc_build_table",
+           "osc_pack_weights_multi", "osc_quant_act_multi", "osc_gemm_multi", "osc_build_table_multi",
+           "osc_status_str", "osc_last_device_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libosc.so is not built ({LIB_PATH}); run python w4a4_outlier_split_amd/build.py")
@@ -48,6 +50,10 @@ _lib.osc_quant_act.argtypes = [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P]
 _lib.osc_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
 _lib.osc_gemm_fp8.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P]
 _lib.osc_build_table.argtypes = [_P, _I, _I, _I, _D, _D, _P, _P, _P, _P]
+_lib.osc_pack_weights_multi.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P]
+_lib.osc_quant_act_multi.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P]
+_lib.osc_gemm_multi.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P]
+_lib.osc_build_table_multi.argtypes = [_P, _I, _I, _I, _D, _D, _I, _P, _P, _P, _P]
 for _f in EXPORTS[:-2]:
     getattr(_lib, _f).restype = _I
 _lib.osc_status_str.argtypes = [_I]
@@ -66,9 +72,10 @@ def scale_bytes(rows: int, H: int, G: int) -> int:
     return rows * (H // G)
 
 
-def side_elems(rows: int, H: int, G: int) -> int:
-    """bf16 elements of a tiled B / W_L buffer: panels of 32 groups, the last one padded."""
-    return rows * ((H // G + 31) // 32) * 32
+def side_elems(rows: int, H: int, G: int, m: int = 1) -> int:
+    """bf16 elements of a tiled B / W_L buffer: m*K compensation columns in panels of 32, the
+    last one padded."""
+    return rows * ((m * (H // G) + 31) // 32) * 32
 
 
 class OscError(RuntimeError):
@@ -138,3 +145,28 @@ def osc_gemm_fp8(QX8, SX, QW, SW, wfmt: int, S: int, N: int, H: int, G: int, Y, 
 def osc_build_table(Xcal, R: int, H: int, G: int, alpha: float, rho: float, L, hits, events, stream=None) -> None:
     _check(_lib.osc_build_table(_ptr(Xcal), R, H, G, float(alpha), float(rho), _ptr(L), _ptr(hits), _ptr(events),
                                 _stream(stream)), "osc_build_table")
+
+
+# ---- several protected channels per group (L: m entries per group, [K, m] or flat K*m)
+
+def osc_pack_weights_multi(W, N: int, H: int, G: int, L, m: int, wfmt: int, QW, SW, WL, stream=None) -> None:
+    keep, lp = _table(L)
+    _check(_lib.osc_pack_weights_multi(_ptr(W), N, H, G, lp, m, wfmt, _ptr(QW), _ptr(SW), _ptr(WL),
+                                       _stream(stream)), "osc_pack_weights_multi")
+
+
+def osc_quant_act_multi(X, S: int, H: int, G: int, L, m: int, afmt: int, QX, SX, B, stream=None) -> None:
+    keep, lp = _table(L)
+    _check(_lib.osc_quant_act_multi(_ptr(X), S, H, G, lp, m, afmt, _ptr(QX), _ptr(SX), _ptr(B), _stream(stream)),
+           "osc_quant_act_multi")
+
+
+def osc_gemm_multi(QX, SX, B, QW, SW, WL, S: int, N: int, H: int, G: int, m: int, Y, yt: int, stream=None) -> None:
+    _check(_lib.osc_gemm_multi(_ptr(QX), _ptr(SX), _ptr(B), _ptr(QW), _ptr(SW), _ptr(WL), S, N, H, G, m, _ptr(Y),
+                               yt, _stream(stream)), "osc_gemm_multi")
+
+
+def osc_build_table_multi(Xcal, R: int, H: int, G: int, alpha: float, rho: float, m: int, L, hits, events,
+                          stream=None) -> None:
+    _check(_lib.osc_build_table_multi(_ptr(Xcal), R, H, G, float(alpha), float(rho), m, _ptr(L), _ptr(hits),
+                                      _ptr(events), _stream(stream)), "osc_build_table_multi")

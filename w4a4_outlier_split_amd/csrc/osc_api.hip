@@ -27,16 +27,23 @@ osc_status check_tiled(int rows, int H, int G) {
   return H % 256 == 0 ? OSC_OK : OSC_E_SHAPE;
 }
 
-// copy the host table slice into the kernel-argument struct, checking every entry
-osc_status pack_table(const int32_t* L, int K, int G, osc::TableArg* t) {
+// copy the host table slice (m entries per group) into the kernel-argument struct, checking
+// every entry and that a group lists each channel at most once
+osc_status pack_table(const int32_t* L, int K, int m, int G, osc::TableArg* t) {
   for (int k = 0; k < K; ++k) {
-    const int32_t v = L[k];
-    if (v < -1 || v >= G) return OSC_E_TABLE;
-    t->v[k] = (int8_t)v;
+    for (int e = 0; e < m; ++e) {
+      const int32_t v = L[k * m + e];
+      if (v < -1 || v >= G) return OSC_E_TABLE;
+      for (int f = 0; f < e; ++f)
+        if (v >= 0 && L[k * m + f] == v) return OSC_E_TABLE;
+      t->v[k * m + e] = (int8_t)v;
+    }
   }
-  for (int k = K; k < OSC_MAX_GROUPS; ++k) t->v[k] = -1;
+  for (int i = K * m; i < OSC_MAX_GROUPS; ++i) t->v[i] = -1;
   return OSC_OK;
 }
+
+bool valid_m(int m) { return m >= 1 && m <= osc::kMaxChannels; }
 
 // the HIP error behind the calling thread's most recent OSC_E_DEVICE
 thread_local hipError_t g_last_error = hipSuccess;
@@ -68,40 +75,52 @@ const char* osc_last_device_error(void) {
   return g_last_error == hipSuccess ? "no device error" : hipGetErrorString(g_last_error);
 }
 
-osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt, void* QX, uint8_t* SX,
-                         void* B, void* stream) {
+osc_status osc_quant_act_multi(const void* X, int S, int H, int G, const int32_t* L, int m, osc_fmt afmt, void* QX,
+                               uint8_t* SX, void* B, void* stream) {
   if (afmt != OSC_MXFP4 && afmt != OSC_MXFP8) return OSC_E_FORMAT;
   osc_status st = check_tiled(S, H, G);
   if (st != OSC_OK) return st;
+  if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
   if (S == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
   if (!X || !QX || !SX) return OSC_E_NULL;
   if ((L == nullptr) != (B == nullptr)) return OSC_E_NULL;
   if (!aligned16(X) || !aligned16(QX) || !aligned16(SX) || (B && !aligned16(B))) return OSC_E_ALIGN;
   osc::TableArg tab;
   if (L) {
-    st = pack_table(L, H / G, G, &tab);
+    st = pack_table(L, H / G, m, G, &tab);
     if (st != OSC_OK) return st;
   }
-  return from_hip(osc::launch_quant(X, S, H, G, L ? &tab : nullptr, L ? osc::kExtractZero : osc::kNoTable, afmt, QX,
-                                    SX, B, static_cast<hipStream_t>(stream)));
+  return from_hip(osc::launch_quant(X, S, H, G, m, L ? &tab : nullptr, L ? osc::kExtractZero : osc::kNoTable, afmt,
+                                    QX, SX, B, static_cast<hipStream_t>(stream)));
 }
 
-osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt, void* QW, uint8_t* SW,
-                            void* WL, void* stream) {
+osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt, void* QX, uint8_t* SX,
+                         void* B, void* stream) {
+  return osc_quant_act_multi(X, S, H, G, L, 1, afmt, QX, SX, B, stream);
+}
+
+osc_status osc_pack_weights_multi(const void* W, int N, int H, int G, const int32_t* L, int m, osc_fmt wfmt, void* QW,
+                                  uint8_t* SW, void* WL, void* stream) {
   if (wfmt != OSC_MXFP4 && wfmt != OSC_MXFP8) return OSC_E_FORMAT;
   osc_status st = check_tiled(N, H, G);
   if (st != OSC_OK) return st;
+  if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
   if (N == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
   if (!W || !QW || !SW) return OSC_E_NULL;
   if ((L == nullptr) != (WL == nullptr)) return OSC_E_NULL;
   if (!aligned16(W) || !aligned16(QW) || !aligned16(SW) || (WL && !aligned16(WL))) return OSC_E_ALIGN;
   osc::TableArg tab;
   if (L) {
-    st = pack_table(L, H / G, G, &tab);
+    st = pack_table(L, H / G, m, G, &tab);
     if (st != OSC_OK) return st;
   }
-  return from_hip(osc::launch_quant(W, N, H, G, L ? &tab : nullptr, L ? osc::kCopyOnly : osc::kNoTable, wfmt, QW, SW,
-                                    WL, static_cast<hipStream_t>(stream)));
+  return from_hip(osc::launch_quant(W, N, H, G, m, L ? &tab : nullptr, L ? osc::kCopyOnly : osc::kNoTable, wfmt, QW,
+                                    SW, WL, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt, void* QW, uint8_t* SW,
+                            void* WL, void* stream) {
+  return osc_pack_weights_multi(W, N, H, G, L, 1, wfmt, QW, SW, WL, stream);
 }
 
 static osc_status check_gemm(int S, int N, int H, int G, osc_ytype yt) {
@@ -111,18 +130,24 @@ static osc_status check_gemm(int S, int N, int H, int G, osc_ytype yt) {
   return OSC_OK;
 }
 
-osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void* QW, const uint8_t* SW,
-                    const void* WL, int S, int N, int H, int G, void* Y, osc_ytype yt, void* stream) {
+osc_status osc_gemm_multi(const void* QX, const uint8_t* SX, const void* B, const void* QW, const uint8_t* SW,
+                          const void* WL, int S, int N, int H, int G, int m, void* Y, osc_ytype yt, void* stream) {
   osc_status st = check_gemm(S, N, H, G, yt);
   if (st != OSC_OK) return st;
+  if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
   if ((B == nullptr) != (WL == nullptr)) return OSC_E_NULL;
-  if (B && (H / G) % 8 != 0) return OSC_E_SHAPE;
+  if (B && ((H / G) * m) % 8 != 0) return OSC_E_SHAPE;
   if (S == 0 || N == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
   if (!QX || !SX || !QW || !SW || !Y) return OSC_E_NULL;
   if (!aligned16(QX) || !aligned16(SX) || !aligned16(QW) || !aligned16(SW) || !aligned16(Y)) return OSC_E_ALIGN;
   if (B && (!aligned16(B) || !aligned16(WL))) return OSC_E_ALIGN;
-  osc::GemmArgs a{QX, SX, B, QW, SW, WL, Y, S, N, H, G, OSC_MXFP4, OSC_MXFP4, yt};
+  osc::GemmArgs a{QX, SX, B, QW, SW, WL, Y, S, N, H, G, B ? (H / G) * m : 0, OSC_MXFP4, OSC_MXFP4, yt};
   return from_hip(osc::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void* QW, const uint8_t* SW,
+                    const void* WL, int S, int N, int H, int G, void* Y, osc_ytype yt, void* stream) {
+  return osc_gemm_multi(QX, SX, B, QW, SW, WL, S, N, H, G, 1, Y, yt, stream);
 }
 
 osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, const uint8_t* SW, osc_fmt wfmt, int S,
@@ -134,20 +159,26 @@ osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, cons
   if (S == 0 || N == 0) return OSC_OK;  // nothing to read or write: pointers are not inspected
   if (!QX8 || !SX || !QW || !SW || !Y) return OSC_E_NULL;
   if (!aligned16(QX8) || !aligned16(SX) || !aligned16(QW) || !aligned16(SW) || !aligned16(Y)) return OSC_E_ALIGN;
-  osc::GemmArgs a{QX8, SX, nullptr, QW, SW, nullptr, Y, S, N, H, G, OSC_MXFP8, wfmt, yt};
+  osc::GemmArgs a{QX8, SX, nullptr, QW, SW, nullptr, Y, S, N, H, G, 0, OSC_MXFP8, wfmt, yt};
   return from_hip(osc::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_build_table_multi(const void* Xcal, int R, int H, int G, double alpha, double rho, int m, int32_t* L,
+                                 int32_t* hits, int32_t* events, void* stream) {
+  if (R <= 0) return OSC_E_SHAPE;
+  osc_status st = check_dims(R, H, G);
+  if (st != OSC_OK) return st;
+  if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
+  if (!(alpha > 0.0) || !(rho > 0.0 && rho <= 1.0)) return OSC_E_SHAPE;
+  if (!Xcal || !L || !hits || !events) return OSC_E_NULL;
+  if (!aligned16(Xcal) || !aligned16(L) || !aligned16(hits) || !aligned16(events)) return OSC_E_ALIGN;
+  return from_hip(osc::launch_build_table(Xcal, R, H, G, m, alpha, rho, L, hits, events,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 osc_status osc_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho, int32_t* L,
                            int32_t* hits, int32_t* events, void* stream) {
-  if (R <= 0) return OSC_E_SHAPE;
-  osc_status st = check_dims(R, H, G);
-  if (st != OSC_OK) return st;
-  if (!(alpha > 0.0) || !(rho > 0.0 && rho <= 1.0)) return OSC_E_SHAPE;
-  if (!Xcal || !L || !hits || !events) return OSC_E_NULL;
-  if (!aligned16(Xcal) || !aligned16(L) || !aligned16(hits) || !aligned16(events)) return OSC_E_ALIGN;
-  return from_hip(osc::launch_build_table(Xcal, R, H, G, alpha, rho, L, hits, events,
-                                          static_cast<hipStream_t>(stream)));
+  return osc_build_table_multi(Xcal, R, H, G, alpha, rho, 1, L, hits, events, stream);
 }
 
 }  // extern "C"

@@ -147,7 +147,7 @@ template <int FA, int FB, int G, bool COMP, int YT, int BM, int BN, int WAVES_M,
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX, const uint8_t* __restrict__ Bc,
     const uint8_t* __restrict__ QW, const uint8_t* __restrict__ SW, const uint8_t* __restrict__ WL,
-    void* __restrict__ Y, int S, int N, int H) {
+    void* __restrict__ Y, int S, int N, int H, int KC) {
   using C = Cfg<FA, FB, G, COMP, BM, BN, WAVES_M, WAVES_N, NS>;
   static_assert(NS >= 3 && NS * C::STAGE <= 160 * 1024, "the LDS ring must hold at least 3 stages");
   static_assert(C::DA * (NS - 2) < 64 && C::DB * (NS - 2) < 64, "vmcnt range");
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   const int n0 = tn * BN;
 
   const int nks = H / C::BK;
-  const int ncs = COMP ? (K + 31) / 32 : 0;  // compensation stages (32 groups each)
+  const int ncs = COMP ? (KC + 31) / 32 : 0;  // compensation stages (32 columns of B / W_L each)
   const int nst = ncs + nks;
 
   // ------------------------------------------------------------ per-lane DMA sources
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const int st = min(st_req, nst - 1);
     const bool comp = COMP && may_comp && st < ncs;
     if (comp) {
-      // compensation panel st; groups past K (last panel) are loaded and zeroed at use
+      // compensation panel st; columns past KC (last panel) are loaded and zeroed at use
       const long off = (long)st * comp_panel;
 #pragma unroll
       for (int i = 0; i < C::NIMAX; ++i)
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const lds_u8* __restrict__ As = smem + (st % NS) * C::STAGE;
     const lds_u8* __restrict__ Bs = As + C::OFF_B;
     if (COMP && comp_stage) {
-      const bool valid = 32 * st + 16 * hf + 8 * h < K;  // chunks past K are zero operands
+      const bool valid = 32 * st + 16 * hf + 8 * h < KC;  // chunks past KC are zero operands
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         const v4i t = lds4(As + arow[i] * 64 + swz<64>(arow[i], 2 * hf + h) * 16);
@@ -578,7 +578,7 @@ hipError_t run(const GemmArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_gemm<FA, FB, G, COMP, YT, BM, BN, WAVES_M, WAVES_N, NS>), dim3(tiles),
                      dim3(WAVES_M * WAVES_N * 64), 0, st, static_cast<const uint8_t*>(a.QX), a.SX,
                      static_cast<const uint8_t*>(a.B), static_cast<const uint8_t*>(a.QW), a.SW,
-                     static_cast<const uint8_t*>(a.WL), a.Y, a.S, a.N, a.H);
+                     static_cast<const uint8_t*>(a.WL), a.Y, a.S, a.N, a.H, a.kc);
   return hipGetLastError();
 }
 

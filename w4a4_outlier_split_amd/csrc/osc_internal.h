@@ -16,13 +16,18 @@ struct TableArg {
 
 enum TableMode { kNoTable = 0, kExtractZero = 1, kCopyOnly = 2 };
 
-// Quantize rows of a bf16 matrix in groups of G (activations or weights).
-//   mode kExtractZero: B[r][k] <- X[r][kG+L[k]], that slot is zeroed before scaling.
-//   mode kCopyOnly:    WL[r][k] <- W[r][kG+L[k]], nothing is zeroed.
-hipError_t launch_quant(const void* X, int rows, int H, int G, const TableArg* tab, int mode, osc_fmt fmt,
+// Most protected channels per group the kernels handle (m = 1 is the single-channel method).
+constexpr int kMaxChannels = 3;
+
+// Quantize rows of a bf16 matrix in groups of G (activations or weights); the table holds m
+// entries per group, entry e of group k at v[k*m + e].
+//   mode kExtractZero: B(r, k*m+e) <- X[r][kG+L[k][e]], those slots are zeroed before scaling.
+//   mode kCopyOnly:    WL(r, k*m+e) <- W[r][kG+L[k][e]], nothing is zeroed.
+hipError_t launch_quant(const void* X, int rows, int H, int G, int m, const TableArg* tab, int mode, osc_fmt fmt,
                         void* Q, uint8_t* SC, void* side, hipStream_t st);
 
-hipError_t launch_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho, int32_t* L,
+// Table slice with up to m entries per group: L and hits device int32[K*m], events int32[K].
+hipError_t launch_build_table(const void* Xcal, int R, int H, int G, int m, double alpha, double rho, int32_t* L,
                               int32_t* hits, int32_t* events, hipStream_t st);
 
 struct GemmArgs {
@@ -34,6 +39,7 @@ struct GemmArgs {
   const void* WL;
   void* Y;
   int S, N, H, G;
+  int kc;  // compensation columns (m*K), 0 without compensation
   osc_fmt afmt, wfmt;
   osc_ytype yt;
 };

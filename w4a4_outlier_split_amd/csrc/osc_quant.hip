@@ -33,7 +33,7 @@ __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf
 
 // One 16-byte chunk c (8 bf16 of one row): extraction, group scale, encoding, tiled stores.
 template <int G, int FMT, int MODE>
-__device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, const TableArg& tab,
+__device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, int m, const TableArg& tab,
                                             uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
                                             uint16_t* __restrict__ side) {
   constexpr int LPG = G / 8;  // lanes per group
@@ -42,33 +42,42 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, con
   constexpr int SPG = G == 16 ? 8 : 4;  // groups per scale panel
   const long code_at = ((long)(col0 >> 7) * rows + r) * 16 + ((col0 & 127) >> 3);  // in 4 / 8-byte units
   const long scale_at = ((long)(k / SPG) * rows + r) * SPG + k % SPG;
-  const long side_at = ((long)(k >> 5) * rows + r) * 32 + (k & 31);
-  uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+  const uint32_t x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];  // as loaded
+  uint32_t w0 = x0, w1 = x1, w2 = x2, w3 = x3;                  // with the listed slots zeroed
 
   if (MODE != kNoTable) {
-    const int ent = tab.v[k];
-    const bool own = ent >= 0 && (ent >> 3) == q;
-    uint32_t val = 0;
-    if (own) {
-      const int e = ent & 7;
-      const uint32_t word = (e >> 1) == 0 ? w0 : (e >> 1) == 1 ? w1 : (e >> 1) == 2 ? w2 : w3;
-      val = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-      if (MODE == kExtractZero) {
-        const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        w0 = (e >> 1) == 0 ? (w0 & keep) : w0;
-        w1 = (e >> 1) == 1 ? (w1 & keep) : w1;
-        w2 = (e >> 1) == 2 ? (w2 & keep) : w2;
-        w3 = (e >> 1) == 3 ? (w3 & keep) : w3;
+    // entries k*m .. k*m+m-1 of the table list distinct channels of group k (or -1); entry e goes
+    // to compensation column k*m + e, written by the lane holding the channel (or lane 0 of the
+    // group, as +0, for -1)
+#pragma unroll
+    for (int e = 0; e < kMaxChannels; ++e) {
+      if (e < m) {
+        const int ent = tab.v[k * m + e];
+        const bool own = ent >= 0 && (ent >> 3) == q;
+        uint32_t val = 0;
+        if (own) {
+          const int c = ent & 7;
+          const uint32_t word = (c >> 1) == 0 ? x0 : (c >> 1) == 1 ? x1 : (c >> 1) == 2 ? x2 : x3;
+          val = (c & 1) ? (word >> 16) : (word & 0xFFFFu);
+          if (MODE == kExtractZero) {
+            const uint32_t keep = (c & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            w0 = (c >> 1) == 0 ? (w0 & keep) : w0;
+            w1 = (c >> 1) == 1 ? (w1 & keep) : w1;
+            w2 = (c >> 1) == 2 ? (w2 & keep) : w2;
+            w3 = (c >> 1) == 3 ? (w3 & keep) : w3;
+          }
+        }
+        const int col = k * m + e;
+        if (own || (ent < 0 && q == 0)) side[((long)(col >> 5) * rows + r) * 32 + (col & 31)] = (uint16_t)val;
       }
     }
-    if (own || (ent < 0 && q == 0)) side[side_at] = (uint16_t)val;
   }
 
   // group amax over the magnitude bits
-  us2 m = __builtin_elementwise_max(as_us2(w0 & 0x7FFF7FFFu), as_us2(w1 & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, as_us2(w2 & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, as_us2(w3 & 0x7FFF7FFFu));
-  int amax = m.x > m.y ? m.x : m.y;
+  us2 mx = __builtin_elementwise_max(as_us2(w0 & 0x7FFF7FFFu), as_us2(w1 & 0x7FFF7FFFu));
+  mx = __builtin_elementwise_max(mx, as_us2(w2 & 0x7FFF7FFFu));
+  mx = __builtin_elementwise_max(mx, as_us2(w3 & 0x7FFF7FFFu));
+  int amax = mx.x > mx.y ? mx.x : mx.y;
   // group max across the LPG adjacent lanes with DPP lane swaps: neighbours (quad_perm 1,0,3,2),
   // pairs (quad_perm 2,3,0,1), then the two quads of an 8-lane row half (half-row mirror)
   amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0xB1, 0xF, 0xF, false));
@@ -107,7 +116,7 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, con
 constexpr int kRowsPerWave = 16;
 
 template <int G, int FMT, int MODE>
-__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int rows, int H, TableArg tab,
+__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int rows, int H, int m, TableArg tab,
                                                uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
                                                uint16_t* __restrict__ side) {
   const int npan = H >> 7;
@@ -129,12 +138,12 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int row
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = r0 + 4 * u;
-    if (r < rows) quant_chunk<G, FMT, MODE>(v[u], r, col0, rows, tab, Q, SC, side);
+    if (r < rows) quant_chunk<G, FMT, MODE>(v[u], r, col0, rows, m, tab, Q, SC, side);
   }
 }
 
 template <int G, int FMT>
-hipError_t dispatch_mode(const void* X, int rows, int H, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+hipError_t dispatch_mode(const void* X, int rows, int H, int m, const TableArg* tab, int mode, void* Q, uint8_t* SC,
                          void* side, hipStream_t st) {
   const long waves = (long)((rows + kRowsPerWave - 1) / kRowsPerWave) * (H >> 7);
   const unsigned grid = (unsigned)((waves + 3) / 4);
@@ -144,27 +153,31 @@ hipError_t dispatch_mode(const void* X, int rows, int H, const TableArg* tab, in
   static const TableArg empty = {};
   const TableArg& t = tab ? *tab : empty;
   if (mode == kExtractZero)
-    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, rows, H, m, t, q, SC, sd);
   else if (mode == kCopyOnly)
-    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, rows, H, m, t, q, SC, sd);
   else
-    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
+    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, rows, H, m, t, q, SC, sd);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t dispatch_fmt(const void* X, int rows, int H, const TableArg* tab, int mode, osc_fmt fmt,
+hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* tab, int mode, osc_fmt fmt,
                         void* Q, uint8_t* SC, void* side, hipStream_t st) {
-  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, rows, H, tab, mode, Q, SC, side, st);
-  return dispatch_mode<G, OSC_MXFP8>(X, rows, H, tab, mode, Q, SC, side, st);
+  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
+  return dispatch_mode<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
 }
 
 // ------------------------------------------------------------------ table builder
-// §3.1 Algorithm 1 for one (position, layer).  One workgroup per group k; threads stride over
-// calibration rows, each row's event is decided in fp64 (sum of G bf16 magnitudes is exact),
-// and channel histograms are accumulated in LDS.
+// §3.1 Algorithm 1 for one (position, layer), with up to m entries per group (m = 1 is the page's
+// single channel; m = 2, 3 the §6 direction).  One workgroup per group k; threads stride over
+// calibration rows.  In each row, each of the m largest |x| (lower channel first among equal
+// magnitudes) that exceeds alpha times the group's mean |x| is an event of its channel, decided
+// in fp64 (the sum of G bf16 magnitudes is formed in channel order); channel histograms are
+// accumulated in LDS.  Entry e is the e-th most frequent event channel (lower channel first on
+// ties) while its count reaches rho * R.
 template <int G>
-__global__ __launch_bounds__(256) void k_build_table(const uint16_t* __restrict__ X, int R, int H, double alpha,
+__global__ __launch_bounds__(256) void k_build_table(const uint16_t* __restrict__ X, int R, int H, int m, double alpha,
                                                      double rho, int32_t* __restrict__ L, int32_t* __restrict__ hits,
                                                      int32_t* __restrict__ events) {
   __shared__ int hist[G];
@@ -176,62 +189,81 @@ __global__ __launch_bounds__(256) void k_build_table(const uint16_t* __restrict_
   int my_events = 0;
   for (int r = threadIdx.x; r < R; r += 256) {
     const uint16_t* row = X + (long)r * H + (long)k * G;
+    float a[G];
     double sum = 0.0;
-    float m = -1.0f;
-    int jr = 0;
     for (int j = 0; j < G; ++j) {
-      const float a = fabsf(__builtin_bit_cast(float, (uint32_t)row[j] << 16));
-      sum += (double)a;
-      if (a > m) {
-        m = a;
-        jr = j;
+      a[j] = fabsf(__builtin_bit_cast(float, (uint32_t)row[j] << 16));
+      sum += (double)a[j];
+    }
+    const double thr = alpha * (sum / G);
+    // the m largest magnitudes, lower channel first on ties
+    int top[kMaxChannels] = {-1, -1, -1};
+    for (int j = 0; j < G; ++j) {
+      int pos = m;
+      for (int e = m - 1; e >= 0; --e)
+        if (top[e] < 0 || a[j] > a[top[e]]) pos = e;
+      if (pos < m) {
+        for (int e = m - 1; e > pos; --e) top[e] = top[e - 1];
+        top[pos] = j;
       }
     }
-    const double mean = sum / G;
-    if ((double)m > alpha * mean) {
-      atomicAdd(&hist[jr], 1);
-      ++my_events;
-    }
+    bool any = false;
+    for (int e = 0; e < m; ++e)
+      if ((double)a[top[e]] > thr) {
+        atomicAdd(&hist[top[e]], 1);
+        any = true;
+      }
+    my_events += any ? 1 : 0;
   }
   atomicAdd(&nev, my_events);
   __syncthreads();
   if (threadIdx.x == 0) {
-    int js = 0;
-    for (int j = 1; j < G; ++j)
-      if (hist[j] > hist[js]) js = j;
-    const int n = nev;
-    hits[k] = n ? hist[js] : 0;
-    events[k] = n;
-    L[k] = (n > 0 && (double)hist[js] >= rho * (double)R) ? js : -1;
+    bool taken[G];
+    for (int j = 0; j < G; ++j) taken[j] = false;
+    bool stop = false;
+    for (int e = 0; e < m; ++e) {
+      int js = -1;
+      for (int j = 0; j < G; ++j)
+        if (!taken[j] && (js < 0 || hist[j] > hist[js])) js = j;
+      taken[js] = true;
+      hits[k * m + e] = hist[js];
+      if (!stop && hist[js] > 0 && (double)hist[js] >= rho * (double)R) {
+        L[k * m + e] = js;
+      } else {
+        stop = true;
+        L[k * m + e] = -1;
+      }
+    }
+    events[k] = nev;
   }
 }
 
 }  // namespace
 
-hipError_t launch_quant(const void* X, int rows, int H, int G, const TableArg* tab, int mode, osc_fmt fmt, void* Q,
-                        uint8_t* SC, void* side, hipStream_t st) {
+hipError_t launch_quant(const void* X, int rows, int H, int G, int m, const TableArg* tab, int mode, osc_fmt fmt,
+                        void* Q, uint8_t* SC, void* side, hipStream_t st) {
   const long nchunks = (long)rows * (H / 8);
   if (nchunks == 0) return hipSuccess;
   switch (G) {
-    case 16: return dispatch_fmt<16>(X, rows, H, tab, mode, fmt, Q, SC, side, st);
-    case 32: return dispatch_fmt<32>(X, rows, H, tab, mode, fmt, Q, SC, side, st);
-    default: return dispatch_fmt<64>(X, rows, H, tab, mode, fmt, Q, SC, side, st);
+    case 16: return dispatch_fmt<16>(X, rows, H, m, tab, mode, fmt, Q, SC, side, st);
+    case 32: return dispatch_fmt<32>(X, rows, H, m, tab, mode, fmt, Q, SC, side, st);
+    default: return dispatch_fmt<64>(X, rows, H, m, tab, mode, fmt, Q, SC, side, st);
   }
 }
 
-hipError_t launch_build_table(const void* Xcal, int R, int H, int G, double alpha, double rho, int32_t* L,
+hipError_t launch_build_table(const void* Xcal, int R, int H, int G, int m, double alpha, double rho, int32_t* L,
                               int32_t* hits, int32_t* events, hipStream_t st) {
   const uint16_t* x = static_cast<const uint16_t*>(Xcal);
   const int K = H / G;
   switch (G) {
     case 16:
-      hipLaunchKernelGGL(k_build_table<16>, dim3(K), dim3(256), 0, st, x, R, H, alpha, rho, L, hits, events);
+      hipLaunchKernelGGL(k_build_table<16>, dim3(K), dim3(256), 0, st, x, R, H, m, alpha, rho, L, hits, events);
       break;
     case 32:
-      hipLaunchKernelGGL(k_build_table<32>, dim3(K), dim3(256), 0, st, x, R, H, alpha, rho, L, hits, events);
+      hipLaunchKernelGGL(k_build_table<32>, dim3(K), dim3(256), 0, st, x, R, H, m, alpha, rho, L, hits, events);
       break;
     default:
-      hipLaunchKernelGGL(k_build_table<64>, dim3(K), dim3(256), 0, st, x, R, H, alpha, rho, L, hits, events);
+      hipLaunchKernelGGL(k_build_table<64>, dim3(K), dim3(256), 0, st, x, R, H, m, alpha, rho, L, hits, events);
       break;
   }
   return hipGetLastError();
