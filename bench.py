@@ -64,13 +64,14 @@ def src_hash(*names):
 class Layer:
     """Device buffers of one OSC linear layer (one buffer set)."""
 
-    def __init__(self, torch, osc, w, L, afmt, wfmt, dev, X_dev=None, packed=None):
+    def __init__(self, torch, osc, w, L, afmt, wfmt, dev, X_dev=None, packed=None, m=1):
         S, H, N, G = w.S, w.H, w.N, w.G
+        self.m = m
         K = H // G
         self.S, self.H, self.N, self.G, self.L, self.afmt, self.wfmt = S, H, N, G, L, afmt, wfmt
         import numpy as np
         u8 = lambda n: torch.empty((n,), dtype=torch.uint8, device=dev)
-        side = lambda R: torch.empty((osc.side_elems(R, H, G),), dtype=torch.int16, device=dev)
+        side = lambda R: torch.empty((osc.side_elems(R, H, G, m),), dtype=torch.int16, device=dev)
         self.X = X_dev if X_dev is not None else torch.from_numpy(w.X.view(np.int16)).to(dev)
         self.QX = u8(osc.code_bytes(S, H, afmt))
         self.SX = u8(osc.scale_bytes(S, H, G))
@@ -80,7 +81,7 @@ class Layer:
             self.QW = u8(osc.code_bytes(N, H, wfmt))
             self.SW = u8(osc.scale_bytes(N, H, G))
             self.WL = side(N) if L is not None else None
-            osc.osc_pack_weights(Wd, N, H, G, L, wfmt, self.QW, self.SW, self.WL)  # offline, untimed
+            osc.osc_pack_weights_multi(Wd, N, H, G, L, m, wfmt, self.QW, self.SW, self.WL)  # offline, untimed
             del Wd
         else:
             self.QW, self.SW, self.WL = (t.clone() if t is not None else None for t in packed)
@@ -135,13 +136,13 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
 
     def quant(l):
         P = l.ptr
-        osc.osc_quant_act(P["X"], l.S, l.H, l.G, l.L, l.afmt, P["QX"], P["SX"], P["B"], s)
+        osc.osc_quant_act_multi(P["X"], l.S, l.H, l.G, l.L, l.m, l.afmt, P["QX"], P["SX"], P["B"], s)
 
     def gemm(l):
         P = l.ptr
         if l.afmt == osc.OSC_MXFP4:
-            osc.osc_gemm(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, P["Y"],
-                         osc.OSC_Y_BF16, s)
+            osc.osc_gemm_multi(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, l.m, P["Y"],
+                               osc.OSC_Y_BF16, s)
         else:
             osc.osc_gemm_fp8(P["QX"], P["SX"], P["QW"], P["SW"], l.wfmt, l.S, l.N, l.H, l.G, P["Y"],
                              osc.OSC_Y_BF16, s)
@@ -172,14 +173,14 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
     return (t1 - t0) / steps, tq, tg
 
 
-def make_sets(torch, osc, w, L, afmt, wfmt, dev):
-    first = Layer(torch, osc, w, L, afmt, wfmt, dev)
+def make_sets(torch, osc, w, L, afmt, wfmt, dev, m=1):
+    first = Layer(torch, osc, w, L, afmt, wfmt, dev, m=m)
     sets = [first]
     per = first.nbytes()
     nsets = max(2, min(16, -(-(MALL_BYTES * 5 // 4) // per)))
     for _ in range(nsets - 1):
         sets.append(Layer(torch, osc, w, L, afmt, wfmt, dev, X_dev=first.X.clone(),
-                          packed=(first.QW, first.SW, first.WL)))
+                          packed=(first.QW, first.SW, first.WL), m=m))
     return sets
 
 
@@ -210,14 +211,28 @@ def table_on_gpu(torch, osc, w, G, dev):
     return out[0].cpu().numpy()
 
 
-def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup):
-    sets = make_sets(torch, osc, w, L, afmt, wfmt, dev)
+def table_on_gpu_multi(torch, osc, w, G, m, dev):
+    import numpy as np
+    K = w.H // G
+    L = torch.empty((K * m,), dtype=torch.int32, device=dev)
+    hits = torch.empty((K * m,), dtype=torch.int32, device=dev)
+    ev = torch.empty((K,), dtype=torch.int32, device=dev)
+    cal = torch.from_numpy(w.calib.view(np.int16)).to(dev)
+    osc.osc_build_table_multi(cal, cal.shape[0], w.H, G, 5.0, 0.35, m, L, hits, ev)
+    torch.cuda.synchronize()
+    return L.cpu().numpy().reshape(K, m)
+
+
+def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1):
+    import numpy as np
+    sets = make_sets(torch, osc, w, L, afmt, wfmt, dev, m)
     wall, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
     flops = 2.0 * w.S * w.H * w.N
     comp = L is not None
     row = {"workload": name, "S": w.S, "H": w.H, "N": w.N, "G": w.G,
            "path": ("osc_mxfp4" if afmt == 0 else ("w8a4_fp8" if wfmt == 0 else "w8a8_fp8")),
-           "protected_groups": None if L is None else int((L >= 0).sum()),
+           "protected_groups": None if L is None else int((np.asarray(L).reshape(-1, m) >= 0).any(axis=1).sum()),
+           "protected_channels": None if L is None else int((np.asarray(L) >= 0).sum()), "m": m,
            "buffer_sets": len(sets), "ms_per_step": wall * 1e3,
            "tflops": flops / wall / 1e12, "t_quant_us": tq * 1e6, "t_gemm_us": tg * 1e6,
            "gemm_tflops": flops / tg / 1e12,
@@ -246,16 +261,19 @@ def quality(torch, osc, w, variants, dev, nrows=32, seed=7):
     Wd = torch.from_numpy(w.W.view(np.int16)).to(dev)
     S, H, N, G = w.S, w.H, w.N, w.G
     u8 = lambda n: torch.empty((n,), dtype=torch.uint8, device=dev)
-    side = lambda R: torch.empty((osc.side_elems(R, H, G),), dtype=torch.int16, device=dev)
     out = {}
-    for name, L, afmt, wfmt in variants:
-        QX, SX, B = u8(osc.code_bytes(S, H, afmt)), u8(osc.scale_bytes(S, H, G)), side(S) if L is not None else None
-        QW, SW, WL = u8(osc.code_bytes(N, H, wfmt)), u8(osc.scale_bytes(N, H, G)), side(N) if L is not None else None
+    for v in variants:
+        name, L, afmt, wfmt = v[:4]
+        m = v[4] if len(v) > 4 else 1
+        QX, SX = u8(osc.code_bytes(S, H, afmt)), u8(osc.scale_bytes(S, H, G))
+        QW, SW = u8(osc.code_bytes(N, H, wfmt)), u8(osc.scale_bytes(N, H, G))
+        B = torch.empty((osc.side_elems(S, H, G, m),), dtype=torch.int16, device=dev) if L is not None else None
+        WL = torch.empty((osc.side_elems(N, H, G, m),), dtype=torch.int16, device=dev) if L is not None else None
         Y = torch.empty((S, N), dtype=torch.float32, device=dev)
-        osc.osc_pack_weights(Wd, N, H, G, L, wfmt, QW, SW, WL)
-        osc.osc_quant_act(Xd, S, H, G, L, afmt, QX, SX, B)
+        osc.osc_pack_weights_multi(Wd, N, H, G, L, m, wfmt, QW, SW, WL)
+        osc.osc_quant_act_multi(Xd, S, H, G, L, m, afmt, QX, SX, B)
         if afmt == osc.OSC_MXFP4:
-            osc.osc_gemm(QX, SX, B, QW, SW, WL, S, N, H, G, Y, osc.OSC_Y_F32)
+            osc.osc_gemm_multi(QX, SX, B, QW, SW, WL, S, N, H, G, m, Y, osc.OSC_Y_F32)
         else:
             osc.osc_gemm_fp8(QX, SX, QW, SW, wfmt, S, N, H, G, Y, osc.OSC_Y_F32)
         torch.cuda.synchronize()
@@ -361,6 +379,14 @@ def main():
                 Ld = table_on_gpu(torch, osc, wdn, 32, dev)
                 rows.append(run_row(torch, osc, "ffn_down_s4096_forced_osc", wdn, Ld, 0, 0, dev, stream, 50, 10))
             del wdn
+        if want("two_outlier"):
+            # the outlook section's case: groups with two persistent channels; one vs two protected
+            wt = synth.two_outlier_groups(S=2048)
+            L1 = table_on_gpu(torch, osc, wt, 32, dev)
+            L2 = table_on_gpu_multi(torch, osc, wt, 32, 2, dev)
+            rows.append(run_row(torch, osc, "two_outlier_s2048_m1", wt, L1, 0, 0, dev, stream, 100, 10))
+            rows.append(run_row(torch, osc, "two_outlier_s2048_m2", wt, L2, 0, 0, dev, stream, 100, 10, m=2))
+            del wt
         for S in (8192, 16):
             for G in (16, 32, 64):
                 n = f"gsweep_s{S}_g{G}"
@@ -378,6 +404,12 @@ def main():
     if args.quality:
         qual = {"qkv_s2048": quality(torch, osc, w, [("osc", L, 0, 0), ("mxfp4_direct", None, 0, 0),
                                                       ("w8a4_fp8", None, 1, 0), ("w8a8", None, 1, 1)], dev)}
+        wt = synth.two_outlier_groups(S=2048)
+        Lt1 = table_on_gpu(torch, osc, wt, 32, dev)
+        Lt2 = table_on_gpu_multi(torch, osc, wt, 32, 2, dev)
+        qual["two_outlier_s2048"] = quality(torch, osc, wt, [("osc_m1", Lt1, 0, 0), ("osc_m2", Lt2, 0, 0, 2),
+                                                              ("mxfp4_direct", None, 0, 0), ("w8a8", None, 1, 1)], dev)
+        del wt
         wdn = synth.ffn_down(S=4096)
         Ld = table_on_gpu(torch, osc, wdn, 32, dev)
         qual["ffn_down_s4096"] = quality(torch, osc, wdn, [("w8a4_fp8", None, 1, 0), ("forced_osc", Ld, 0, 0),
