@@ -173,6 +173,45 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
     return (t1 - t0) / steps, tq, tg
 
 
+def time_layer_graph(torch, osc, sets, reps, stream):
+    """For launch-bound rows (a few microseconds of GPU work per kernel, less than the host
+    needs to enqueue one): capture reps steps (rotating over the buffer sets) into one HIP
+    graph, and reps quantizations / reps GEMMs into two more, and time one replay of each.
+    Returns seconds per step, per quantization and per GEMM."""
+    def quant(l, s):
+        P = l.ptr
+        osc.osc_quant_act_multi(P["X"], l.S, l.H, l.G, l.L, l.m, l.afmt, P["QX"], P["SX"], P["B"], s)
+
+    def gemm(l, s):
+        P = l.ptr
+        if l.afmt == osc.OSC_MXFP4:
+            osc.osc_gemm_multi(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, l.m, P["Y"],
+                               osc.OSC_Y_BF16, s)
+        else:
+            osc.osc_gemm_fp8(P["QX"], P["SX"], P["QW"], P["SW"], l.wfmt, l.S, l.N, l.H, l.G, P["Y"],
+                             osc.OSC_Y_BF16, s)
+
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(reps):
+                body(sets[i % len(sets)], cs)
+        return g
+
+    graphs = [capture(lambda l, cs: (quant(l, cs), gemm(l, cs))), capture(quant), capture(gemm)]
+    out = []
+    for g in graphs:
+        g.replay()  # warm
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        out.append((time.perf_counter() - t0) / reps)
+    del graphs
+    return tuple(out)
+
+
 def make_sets(torch, osc, w, L, afmt, wfmt, dev, m=1):
     first = Layer(torch, osc, w, L, afmt, wfmt, dev, m=m)
     sets = [first]
@@ -226,14 +265,18 @@ def table_on_gpu_multi(torch, osc, w, G, m, dev):
 def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1):
     import numpy as np
     sets = make_sets(torch, osc, w, L, afmt, wfmt, dev, m)
-    wall, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
+    graphed = w.S <= 32  # decode shapes: kernels shorter than the host's enqueue time
+    if graphed:
+        wall, tq, tg = time_layer_graph(torch, osc, sets, steps, stream)
+    else:
+        wall, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
     flops = 2.0 * w.S * w.H * w.N
     comp = L is not None
     row = {"workload": name, "S": w.S, "H": w.H, "N": w.N, "G": w.G,
            "path": ("osc_mxfp4" if afmt == 0 else ("w8a4_fp8" if wfmt == 0 else "w8a8_fp8")),
            "protected_groups": None if L is None else int((np.asarray(L).reshape(-1, m) >= 0).any(axis=1).sum()),
            "protected_channels": None if L is None else int((np.asarray(L) >= 0).sum()), "m": m,
-           "buffer_sets": len(sets), "ms_per_step": wall * 1e3,
+           "buffer_sets": len(sets), "timing": "hip_graph" if graphed else "eager", "ms_per_step": wall * 1e3,
            "tflops": flops / wall / 1e12, "t_quant_us": tq * 1e6, "t_gemm_us": tg * 1e6,
            "gemm_tflops": flops / tg / 1e12,
            "quant_gbs": quant_bytes(w, afmt, comp) / tq / 1e9,

@@ -305,3 +305,38 @@ def test_gemm_fp8_ragged(S, N, H, G, wfmt):
     rq, rs, _ = oracle.quant_act(X, G, None, FP8)
     wq, ws, _ = oracle.pack_weights(W, G, None, wfmt)
     assert_y_close(host_y(Y), oracle.gemm(rq, rs, wq, ws, G, afmt=FP8, wfmt=wfmt), what=f"fp8 {S}x{N}x{H}")
+
+
+# ------------------------------------------------------------------ skinny-S (decode) kernel
+
+@pytest.mark.parametrize("S", [1, 17, 32])
+@pytest.mark.parametrize("G,comp", [(16, True), (32, True), (32, False), (64, True)])
+def test_gemm_decode_kernel(S, G, comp):
+    """S <= 32 runs the skinny-S kernel (K split over the waves of a 32-column block)."""
+    N, H = 300, 1536  # ragged last column block; 12 main stages over 8 waves
+    X = synth.random_bf16((S, H), seed=S * 7 + G, scale=2.0)
+    W = synth.random_bf16((N, H), seed=G + 3, scale=0.05)
+    L = np.random.default_rng(S + G).integers(-1, G, H // G).astype(np.int32) if comp else None
+    QX, SX, B = quant(dev_bits16(X), S, H, G, L, FP4)
+    QW, SW, WL = pack(dev_bits16(W), N, H, G, L, FP4)
+    Y = gemm(QX, SX, B, QW, SW, WL, S, N, H, G)
+    Yb = gemm(QX, SX, B, QW, SW, WL, S, N, H, G, osc.OSC_Y_BF16)
+    torch.cuda.synchronize()
+    ref = oracle.osc_linear(X, W, G, L) if comp else oracle.gemm(*oracle.quant_act(X, G, None)[:2],
+                                                                *oracle.pack_weights(W, G, None)[:2], G)
+    assert_y_close(host_y(Y), ref, what=f"decode S={S} G={G} comp={comp}")
+    assert torch.equal(Yb.view(torch.int16), Y.to(torch.bfloat16).view(torch.int16))
+
+
+@pytest.mark.parametrize("S,wfmt,G", [(16, FP4, 32), (7, FP8, 64), (32, FP4, 64)])
+def test_gemm_fp8_decode_kernel(S, wfmt, G):
+    N, H = 200, 1536
+    X = synth.random_bf16((S, H), seed=S + 11, scale=2.0)
+    W = synth.random_bf16((N, H), seed=N + 12, scale=0.05)
+    QX, SX, _ = quant(dev_bits16(X), S, H, G, None, FP8)
+    QW, SW, _ = pack(dev_bits16(W), N, H, G, None, wfmt)
+    Y = gemm_fp8(QX, SX, QW, SW, wfmt, S, N, H, G)
+    torch.cuda.synchronize()
+    rq, rs, _ = oracle.quant_act(X, G, None, FP8)
+    wq, ws, _ = oracle.pack_weights(W, G, None, wfmt)
+    assert_y_close(host_y(Y), oracle.gemm(rq, rs, wq, ws, G, afmt=FP8, wfmt=wfmt), what=f"fp8 decode S={S}")

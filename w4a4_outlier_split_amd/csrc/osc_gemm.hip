@@ -617,6 +617,7 @@ hipError_t pick_nocomp(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.S == 0 || a.N == 0) return hipSuccess;
+  if (a.S <= kDecodeRows) return launch_gemm_dec(a, st);
   if (a.afmt == OSC_MXFP4) {
     switch (a.G) {
       case 16: return pick_comp<kFp4, kFp4, 16>(a, st);

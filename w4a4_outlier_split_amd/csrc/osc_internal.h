@@ -46,4 +46,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
+// S <= 32 rows: the skinny-S kernel (one 32-column block per workgroup, K split over its waves).
+constexpr int kDecodeRows = 32;
+hipError_t launch_gemm_dec(const GemmArgs& a, hipStream_t st);
+
 }  // namespace osc
