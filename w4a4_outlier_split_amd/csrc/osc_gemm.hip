@@ -583,19 +583,22 @@ hipError_t run(const GemmArgs& a, hipStream_t st) {
 }
 
 // Tile choice per shape (the MI355X reading of the page's "adaptive resource scheduling",
-// §3.3): the largest tile that still yields enough tiles to cover the 256 CUs.  256x256 and
-// 256x192 only where their wavefront sub-tiles fit the register file without spilling (E2M1
-// operands with G = 32 or 64); G = 16 and E4M3 activations use 256x128.
+// §3.3): the largest tile that still gives (nearly) every one of the 256 CUs a tile.  A CU takes
+// in ~30 bytes of operands per clock at most, so bigger tiles (fewer operand bytes per flop) win
+// whenever they still cover the chip: 256x256 needs ~34 B/clk of E2M1 at the MFMA rate, 256x192
+// ~40, 256x128 ~51.  With E4M3 activations against E4M3 weights a 256-wide stage does not fit
+// three times in LDS; those stay at 256x128.
 template <int FA, int FB, int G, bool COMP, int YT>
 hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
+  constexpr long kCover = 240;  // tiles that count as covering the 256 CUs
   auto tiles = [&](int bm, int bn) { return (long)((a.S + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  constexpr bool big = FA == kFp4 && FB == kFp4 && G != 16;
-  if constexpr (big) {
-    if (tiles(256, 256) >= 512) return run<FA, FB, G, COMP, YT, 256, 256, 4, 2>(a, st);
-    if (a.N % 192 == 0 && tiles(256, 192) >= 200) return run<FA, FB, G, COMP, YT, 256, 192, 4, 2>(a, st);
+  constexpr bool wide = !(FA == kFp8 && FB == kFp8);
+  if constexpr (wide) {
+    if (tiles(256, 256) >= kCover) return run<FA, FB, G, COMP, YT, 256, 256, 4, 2>(a, st);
+    if (a.N % 192 == 0 && tiles(256, 192) >= kCover) return run<FA, FB, G, COMP, YT, 256, 192, 4, 2>(a, st);
   }
-  if (tiles(256, 128) >= 200) return run<FA, FB, G, COMP, YT, 256, 128, 4, 2>(a, st);
-  if (tiles(128, 128) >= 200) return run<FA, FB, G, COMP, YT, 128, 128, 4, 2>(a, st);
+  if (tiles(256, 128) >= kCover) return run<FA, FB, G, COMP, YT, 256, 128, 4, 2>(a, st);
+  if (tiles(128, 128) >= kCover) return run<FA, FB, G, COMP, YT, 128, 128, 4, 2>(a, st);
   return run<FA, FB, G, COMP, YT, 64, 64, 2, 2>(a, st);
 }
 
