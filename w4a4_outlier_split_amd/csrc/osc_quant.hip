@@ -5,10 +5,10 @@
 //
 // Data flow: HBM-bound.  Outputs go to the tiled layout the GEMM streams: codes in panels of
 // 128 channels (R rows x 64 or 128 bytes), scales in panels of 4 groups (8 when G = 16), B / W_L
-// in panels of 32 groups.  A wavefront owns 16 rows x one 128-channel panel: per load
+// in panels of 32 groups.  A wavefront owns 8 rows x one 128-channel panel: per load
 // instruction, 16 lanes cover one row's 256 bytes of the panel (G/8 adjacent lanes form a
-// group) and 4 rows are covered at once; all four loads are issued before any is processed.
-// Its code output is then one contiguous 1 KiB (2 KiB for E4M3) block of the panel.  The group amax is
+// group) and 4 rows are covered at once; both loads are issued before either is processed.
+// Its code output is then one contiguous 512-byte (1 KiB for E4M3) block of the panel.  The group amax is
 // an integer max over the bf16 magnitude bits (|x| ordering == bit ordering for finite values),
 // reduced across the group's lanes with cross-lane swizzles.  The E8M0 code is read straight
 // off the amax exponent field: floor(log2 amax) - emax + 127 = E - 2 (E2M1) or E - 8 (E4M3),
@@ -32,8 +32,8 @@ __device__ __forceinline__ uint32_t as_u32(us2 v) { return __builtin_bit_cast(ui
 __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
 
 // One 16-byte chunk c (8 bf16 of one row): extraction, group scale, encoding, tiled stores.
-template <int G, int FMT, int MODE>
-__device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, int m, const TableArg& tab,
+template <int G, int FMT, int MODE, int M>
+__device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, const TableArg& tab,
                                             uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
                                             uint16_t* __restrict__ side) {
   constexpr int LPG = G / 8;  // lanes per group
@@ -50,9 +50,9 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, int
     // to compensation column k*m + e, written by the lane holding the channel (or lane 0 of the
     // group, as +0, for -1)
 #pragma unroll
-    for (int e = 0; e < kMaxChannels; ++e) {
-      if (e < m) {
-        const int ent = tab.v[k * m + e];
+    for (int e = 0; e < M; ++e) {
+      {
+        const int ent = tab.v[k * M + e];
         const bool own = ent >= 0 && (ent >> 3) == q;
         uint32_t val = 0;
         if (own) {
@@ -67,7 +67,7 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, int
             w3 = (c >> 1) == 3 ? (w3 & keep) : w3;
           }
         }
-        const int col = k * m + e;
+        const int col = k * M + e;
         if (own || (ent < 0 && q == 0)) side[((long)(col >> 5) * rows + r) * 32 + (col & 31)] = (uint16_t)val;
       }
     }
@@ -113,10 +113,10 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, int
   }
 }
 
-constexpr int kRowsPerWave = 16;
+constexpr int kRowsPerWave = 8;
 
-template <int G, int FMT, int MODE>
-__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int rows, int H, int m, TableArg tab,
+template <int G, int FMT, int MODE, int M>
+__global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int rows, int H, TableArg tab,
                                                uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
                                                uint16_t* __restrict__ side) {
   const int npan = H >> 7;
@@ -129,17 +129,29 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int row
   const int col0 = p * 128 + cc * 8;
   const int r0 = rb * kRowsPerWave + (lane >> 4);
   // rows past the end are skipped by whole 16-lane row segments, so a group's lanes agree
-  u4 v[4];
+  constexpr int U = kRowsPerWave / 4;
+  u4 v[U];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int r = r0 + 4 * u;
     if (r < rows) v[u] = __builtin_nontemporal_load(X + (long)r * (H >> 3) + (col0 >> 3));
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int r = r0 + 4 * u;
-    if (r < rows) quant_chunk<G, FMT, MODE>(v[u], r, col0, rows, m, tab, Q, SC, side);
+    if (r < rows) quant_chunk<G, FMT, MODE, M>(v[u], r, col0, rows, tab, Q, SC, side);
   }
+}
+
+template <int G, int FMT, int MODE>
+hipError_t launch_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC, uint16_t* sd,
+                    unsigned grid, hipStream_t st) {
+  switch (m) {
+    case 1: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 2: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 2>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    default: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 3>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+  }
+  return hipGetLastError();
 }
 
 template <int G, int FMT>
@@ -152,12 +164,9 @@ hipError_t dispatch_mode(const void* X, int rows, int H, int m, const TableArg* 
   uint16_t* sd = static_cast<uint16_t*>(side);
   static const TableArg empty = {};
   const TableArg& t = tab ? *tab : empty;
-  if (mode == kExtractZero)
-    hipLaunchKernelGGL((k_quant<G, FMT, kExtractZero>), dim3(grid), dim3(256), 0, st, x, rows, H, m, t, q, SC, sd);
-  else if (mode == kCopyOnly)
-    hipLaunchKernelGGL((k_quant<G, FMT, kCopyOnly>), dim3(grid), dim3(256), 0, st, x, rows, H, m, t, q, SC, sd);
-  else
-    hipLaunchKernelGGL((k_quant<G, FMT, kNoTable>), dim3(grid), dim3(256), 0, st, x, rows, H, m, t, q, SC, sd);
+  if (mode == kExtractZero) return launch_m<G, FMT, kExtractZero>(x, rows, H, m, t, q, SC, sd, grid, st);
+  if (mode == kCopyOnly) return launch_m<G, FMT, kCopyOnly>(x, rows, H, m, t, q, SC, sd, grid, st);
+  hipLaunchKernelGGL((k_quant<G, FMT, kNoTable, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   return hipGetLastError();
 }
 
