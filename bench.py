@@ -40,8 +40,8 @@ MALL_BYTES = 256 << 20
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=2000, help="untimed steps first (~0.1 s: clocks settle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the extra workload rows")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -390,7 +390,7 @@ def main():
     comparator = None
     if args.only in (None, "w8a8"):
         r8 = run_row(torch, osc, "qkv_proj_s2048_w8a8", w, None, osc.OSC_MXFP8, osc.OSC_MXFP8, dev, stream,
-                     max(20, args.steps // 2), args.warmup)
+                     max(20, args.steps // 2), args.warmup // 2)
         rows.append(r8)
         if head is not None:
             comparator = {"w8a8_ms_per_step": r8["ms_per_step"], "osc_ms_per_step": head["ms_per_step"],
@@ -404,8 +404,8 @@ def main():
             wf = synth.ffn_up(S=4096)
             Lf = table_on_gpu(torch, osc, wf, 32, dev)
             if want("ffn_up_s4096"):
-                ru = run_row(torch, osc, "ffn_up_s4096_g32", wf, Lf, 0, 0, dev, stream, 50, 10)
-                r8 = run_row(torch, osc, "ffn_up_s4096_w8a8", wf, None, 1, 1, dev, stream, 50, 10)
+                ru = run_row(torch, osc, "ffn_up_s4096_g32", wf, Lf, 0, 0, dev, stream, 100, 200)
+                r8 = run_row(torch, osc, "ffn_up_s4096_w8a8", wf, None, 1, 1, dev, stream, 100, 200)
                 r8["osc_speedup_vs_w8a8"] = r8["ms_per_step"] / ru["ms_per_step"]
                 rows += [ru, r8]
             if want("ffn_up_s16"):
@@ -417,18 +417,18 @@ def main():
         if want("ffn_down_fp8") or want("ffn_down_osc"):
             wdn = synth.ffn_down(S=4096)
             if want("ffn_down_fp8"):
-                rows.append(run_row(torch, osc, "ffn_down_s4096_fp8_w4a8", wdn, None, 1, 0, dev, stream, 50, 10))
+                rows.append(run_row(torch, osc, "ffn_down_s4096_fp8_w4a8", wdn, None, 1, 0, dev, stream, 100, 200))
             if want("ffn_down_osc"):
                 Ld = table_on_gpu(torch, osc, wdn, 32, dev)
-                rows.append(run_row(torch, osc, "ffn_down_s4096_forced_osc", wdn, Ld, 0, 0, dev, stream, 50, 10))
+                rows.append(run_row(torch, osc, "ffn_down_s4096_forced_osc", wdn, Ld, 0, 0, dev, stream, 100, 200))
             del wdn
         if want("two_outlier"):
             # the outlook section's case: groups with two persistent channels; one vs two protected
             wt = synth.two_outlier_groups(S=2048)
             L1 = table_on_gpu(torch, osc, wt, 32, dev)
             L2 = table_on_gpu_multi(torch, osc, wt, 32, 2, dev)
-            rows.append(run_row(torch, osc, "two_outlier_s2048_m1", wt, L1, 0, 0, dev, stream, 100, 10))
-            rows.append(run_row(torch, osc, "two_outlier_s2048_m2", wt, L2, 0, 0, dev, stream, 100, 10, m=2))
+            rows.append(run_row(torch, osc, "two_outlier_s2048_m1", wt, L1, 0, 0, dev, stream, 500, 1000))
+            rows.append(run_row(torch, osc, "two_outlier_s2048_m2", wt, L2, 0, 0, dev, stream, 500, 1000, m=2))
             del wt
         for S in (8192, 16):
             for G in (16, 32, 64):
@@ -437,7 +437,7 @@ def main():
                     continue
                 ws = synth.group_sweep(S, G)
                 Ls = table_on_gpu(torch, osc, ws, G, dev)
-                r = run_row(torch, osc, n, ws, Ls, 0, 0, dev, stream, 50 if S > 16 else 200, 10)
+                r = run_row(torch, osc, n, ws, Ls, 0, 0, dev, stream, 100 if S > 16 else 200, 200)
                 if S == 16:
                     r["gemm_frac_of_hbm"] = r["gemm_gbs"] / PEAK_HBM_GBS
                 rows.append(r)
