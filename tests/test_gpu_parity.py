@@ -340,3 +340,31 @@ def test_gemm_fp8_decode_kernel(S, wfmt, G):
     rq, rs, _ = oracle.quant_act(X, G, None, FP8)
     wq, ws, _ = oracle.pack_weights(W, G, None, wfmt)
     assert_y_close(host_y(Y), oracle.gemm(rq, rs, wq, ws, G, afmt=FP8, wfmt=wfmt), what=f"fp8 decode S={S}")
+
+
+@pytest.mark.parametrize("S,N,H,G", [(1024, 8192, 1024, 32),   # 256x128 tiles
+                                     (512, 8192, 512, 64),     # 128x128 tiles
+                                     (2048, 6144, 1024, 16)])  # 256x192 tiles at G=16
+def test_gemm_every_tile_shape(S, N, H, G):
+    """Shapes that make the tile choice pick each prefill configuration; sampled rows x all columns
+    and all rows x sampled columns against the oracle."""
+    X = synth.random_bf16((S, H), seed=S + H, scale=2.0)
+    W = synth.random_bf16((N, H), seed=N + H, scale=0.05)
+    L = np.random.default_rng(G + H).integers(-1, G, H // G).astype(np.int32)
+    QX, SX, B = quant(dev_bits16(X), S, H, G, L, FP4)
+    QW, SW, WL = pack(dev_bits16(W), N, H, G, L, FP4)
+    Y = gemm(QX, SX, B, QW, SW, WL, S, N, H, G)
+    torch.cuda.synchronize()
+    got = host_y(Y)
+    rows = sample_rows(S, 12, 31)
+    cols = sample_rows(N, 12, 32)
+    wide = sample_rows(N, 1024, 33)
+    rq, rs, rb = oracle.quant_act(X[rows], G, L, FP4)
+    wq, ws, wl = oracle.pack_weights(W[wide], G, L, FP4)
+    ref_rows = oracle.gemm(rq, rs, wq, ws, G, rb, wl)
+    xq, xs, xb = oracle.quant_act(X, G, L, FP4)
+    cq, cs, cl = oracle.pack_weights(W[cols], G, L, FP4)
+    ref_cols = oracle.gemm(xq, xs, cq, cs, G, xb, cl)
+    rms = float(np.sqrt(np.mean(ref_rows ** 2)))
+    assert_y_close(got[np.ix_(rows, wide)], ref_rows, rms, what=f"{S}x{N}x{H} G={G} rows")
+    assert_y_close(got[:, cols], ref_cols, rms, what=f"{S}x{N}x{H} G={G} cols")
