@@ -9,9 +9,11 @@ same accumulators), on the Qwen3-8B QKV projection shape S=2048, H=4096, N=6144,
 offline (§3.3) and untimed.  Inputs are resident in HBM before the timed region; the
 steps rotate over buffer sets whose total exceeds the 256 MB Infinity Cache.
 
-metric: TFLOP/s = 2*S*H*N / (t_quant + t_gemm), from the wall clock of K steps
-bracketed by device synchronisation.  The GEMM's average kernel duration is measured
-with HIP events on the stream the kernels run on, for the roofline object.  Those events
+metric: TFLOP/s = 2*S*H*N / (t_quant + t_gemm), from one HIP event pair around K steps run
+back to back on one stream (the host clock around the same K steps, bracketed by device
+synchronisation, is reported beside it).  A second pass with an event between the two kernels
+of every step gives the quant / GEMM split; the GEMM's average duration feeds the roofline
+object.  All events are recorded on the stream the kernels run on.  Those events
 are created with hipEventDisableSystemFence: a default event's system-scope release
 writes the L2 back to memory when it is recorded, which would be charged to the kernels
 around it (and to the step).  The CPU
@@ -130,8 +132,10 @@ class TimingEvents:
 
 
 def time_layer(torch, osc, sets, steps, warmup, stream):
-    """Run quant + GEMM over rotating buffer sets.  Returns wall seconds per step and the
-    average event-timed durations of the quant and GEMM kernels inside the timed region."""
+    """Run quant + GEMM over rotating buffer sets.  The steps run back to back under one event
+    pair (the step time); a second pass with an event between the two kernels of every step gives
+    the quant / GEMM split.  Returns seconds per step (events), seconds per step (host clock around
+    the first pass) and the average event-timed durations of the quant and GEMM kernels."""
     s = stream.cuda_stream
 
     def quant(l):
@@ -152,11 +156,21 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
             l = sets[i % len(sets)]
             quant(l)
             gemm(l)
-        ev = TimingEvents(2 * steps + 1)
+        ev = TimingEvents(2 * steps + 3)
         gc.collect()
         gc.disable()  # no collector pause inside the timed region
+        # pass 1: the step time, steps back to back
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        ev.record(2 * steps + 1, s)
+        for i in range(steps):
+            l = sets[i % len(sets)]
+            quant(l)
+            gemm(l)
+        ev.record(2 * steps + 2, s)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        # pass 2: the split between the two kernels
         for i in range(steps):
             l = sets[i % len(sets)]
             ev.record(2 * i, s)
@@ -165,12 +179,12 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
             gemm(l)
         ev.record(2 * steps, s)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         gc.enable()
+    t_step = ev.ms(2 * steps + 1, 2 * steps + 2) / steps * 1e-3
     tq = sum(ev.ms(2 * i, 2 * i + 1) for i in range(steps)) / steps * 1e-3
     tg = sum(ev.ms(2 * i + 1, 2 * i + 2) for i in range(steps)) / steps * 1e-3
     ev.close()
-    return (t1 - t0) / steps, tq, tg
+    return t_step, (t1 - t0) / steps, tq, tg
 
 
 def time_layer_graph(torch, osc, sets, reps, stream):
@@ -268,8 +282,9 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1)
     graphed = w.S <= 32  # decode shapes: kernels shorter than the host's enqueue time
     if graphed:
         wall, tq, tg = time_layer_graph(torch, osc, sets, steps, stream)
+        host = wall
     else:
-        wall, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
+        wall, host, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
     flops = 2.0 * w.S * w.H * w.N
     comp = L is not None
     row = {"workload": name, "S": w.S, "H": w.H, "N": w.N, "G": w.G,
@@ -277,6 +292,7 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1)
            "protected_groups": None if L is None else int((np.asarray(L).reshape(-1, m) >= 0).any(axis=1).sum()),
            "protected_channels": None if L is None else int((np.asarray(L) >= 0).sum()), "m": m,
            "buffer_sets": len(sets), "timing": "hip_graph" if graphed else "eager", "ms_per_step": wall * 1e3,
+           "host_ms_per_step": host * 1e3,
            "tflops": flops / wall / 1e12, "t_quant_us": tq * 1e6, "t_gemm_us": tg * 1e6,
            "gemm_tflops": flops / tg / 1e12,
            "quant_gbs": quant_bytes(w, afmt, comp) / tq / 1e9,

@@ -93,7 +93,7 @@ typedef enum {
  *   WL  bf16, tiled (R = N), device, written: WL(n, k) = W[n][k*G + L[k]], or +0
  *       when L[k] = -1.  This is the page's K x N slice W_L stored output-major.
  * Constraints: N >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS,
- * N * H < 2^34.
+ * N < 2^24, N * H < 2^34.
  */
 osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L, osc_fmt wfmt,
                             void* QW, uint8_t* SW, void* WL, void* stream);
@@ -109,7 +109,7 @@ osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L
  *   B   bf16, tiled (R = S), device, written: B(s, k) = X[s][k*G + L[k]] bit for
  *       bit, or +0 when L[k] = -1.
  * Constraints: S >= 0, G in {16, 32, 64}, H > 0, H % 256 == 0, K <= OSC_MAX_GROUPS,
- * S * H < 2^34.
+ * S < 2^24, S * H < 2^34.
  */
 osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, osc_fmt afmt,
                          void* QX, uint8_t* SX, void* B, void* stream);
@@ -124,7 +124,7 @@ osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, o
  *   B, WL  both NULL for a plain MXFP4 GEMM (no compensation), else both set.
  *   Y   [S][N], bf16 or fp32 per yt, device, written.
  * Constraints: S >= 0, N >= 0, G in {16, 32, 64}, H % 256 == 0, K <= OSC_MAX_GROUPS,
- * and with compensation K % 8 == 0.
+ * S, N < 2^24, S * H and N * H < 2^34, and with compensation K % 8 == 0.
  */
 osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void* QW,
                     const uint8_t* SW, const void* WL, int S, int N, int H, int G, void* Y,
@@ -135,7 +135,8 @@ osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void
  * (tiled, from osc_quant_act with afmt = OSC_MXFP8, L = NULL) and weights in wfmt (OSC_MXFP4,
  * the default W4A8 reading, or OSC_MXFP8); no extraction, no compensation.
  *   Y   [S][N], bf16 or fp32 per yt, device, written.
- * Constraints: S >= 0, N >= 0, G in {32, 64}, H % 256 == 0, K <= OSC_MAX_GROUPS.
+ * Constraints: S >= 0, N >= 0, G in {32, 64}, H % 256 == 0, K <= OSC_MAX_GROUPS,
+ * S, N < 2^24, S * H and N * H < 2^34.
  */
 osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, const uint8_t* SW,
                         osc_fmt wfmt, int S, int N, int H, int G, void* Y, osc_ytype yt,

@@ -54,6 +54,8 @@ def test_quant_act_validation():
     assert q(H=250) == 2                     # H % G != 0
     assert q(H=384) == 2                     # tiled layout: H % 256 != 0
     assert q(S=1 << 22, H=4096) == 2         # S * H >= 2^34
+    assert q(S=1 << 24, H=256) == 2          # S >= 2^24 (32-bit panel offsets)
+    assert q(S=(1 << 24) - 1, H=256, X=U) == 4  # the largest S passes the shape checks
     assert q(S=-1) == 2
     assert q(X=None) == 1 and q(QX=None) == 1 and q(SX=None) == 1
     assert q(B=None) == 1                    # table given but no B
@@ -74,6 +76,7 @@ def test_pack_weights_validation():
     assert p(W=U) == 4 and p(SW=U) == 4
     assert p(N=-3) == 2
     assert p(H=384) == 2
+    assert p(N=1 << 24) == 2
     bad, bp = L8([3, 3, 3, 3, 3, 3, 3, 40])
     assert p(l=bp) == 3
 
@@ -89,6 +92,8 @@ def test_gemm_validation():
     assert g(Y=U) == 4 and g(WL=U) == 4
     assert g(S=-1) == 2 and g(N=-1) == 2
     assert g(S=0) == 0 and g(N=0) == 0       # valid, nothing launched
+    assert g(S=1 << 24) == 2 and g(N=1 << 24) == 2          # rows >= 2^24
+    assert g(S=1 << 22, H=4096) == 2 and g(N=1 << 22, H=4096) == 2  # rows * H >= 2^34
 
 
 def test_gemm_fp8_validation():

@@ -24,6 +24,7 @@ osc_status check_tiled(int rows, int H, int G) {
   const osc_status st = check_dims(rows, H, G);
   if (st != OSC_OK) return st;
   if ((long long)rows * (H / 8) > 0x7FFFFFFFLL) return OSC_E_SHAPE;  // 16-byte chunks indexed in 32 bits
+  if (rows >= (1 << 24)) return OSC_E_SHAPE;  // byte offsets inside one operand panel fit in 31 bits
   return H % 256 == 0 ? OSC_OK : OSC_E_SHAPE;
 }
 
@@ -127,6 +128,9 @@ static osc_status check_gemm(int S, int N, int H, int G, osc_ytype yt) {
   if (yt != OSC_Y_BF16 && yt != OSC_Y_F32) return OSC_E_FORMAT;
   if (S < 0 || N < 0 || H <= 0 || !valid_g(G) || H % 256 != 0) return OSC_E_SHAPE;
   if (H / G > OSC_MAX_GROUPS) return OSC_E_SHAPE;
+  // the operands obey the limits of the calls that wrote them
+  if (S >= (1 << 24) || N >= (1 << 24)) return OSC_E_SHAPE;
+  if ((long long)S * (H / 8) > 0x7FFFFFFFLL || (long long)N * (H / 8) > 0x7FFFFFFFLL) return OSC_E_SHAPE;
   return OSC_OK;
 }
 

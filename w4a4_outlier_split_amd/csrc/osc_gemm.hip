@@ -90,11 +90,16 @@ struct Interleave {
   }
 };
 
-__device__ __forceinline__ void dma16(const void* g, lds_u8* __restrict__ l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+// LDS-DMA through a buffer resource: the resource (scalar registers) holds the panel base, the
+// lane supplies a 32-bit offset.  Word 3 selects the 32-bit data format that raw loads need.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const uint8_t* base, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, lds_u8* __restrict__ l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_u8* __restrict__ l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_u8* __restrict__ l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, off, 0, 0, 0);
 }
 
 template <int FA, int FB, int G, bool COMP, int BM, int BN, int WAVES_M, int WAVES_N, int NS>
@@ -134,7 +139,7 @@ struct Cfg {
   static constexpr int STAGE = OFF_SB + SROWS_B * SBL;
   static constexpr int NMF = (G == 16) ? 4 : 2;    // scaled MFMAs per stage per block
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert(!COMP || FA == kFp4, "compensation stages reuse the 64-byte E2M1 row geometry");
+  static_assert(!COMP || (FA == kFp4 && FB == kFp4), "compensation stages reuse the 64-byte E2M1 row geometry");
 };
 
 template <int FA, int FB, int G, int BM, int BN, int WAVES_M, int WAVES_N>
@@ -198,12 +203,15 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   const int dst_scale = xside ? C::OFF_SA : C::OFF_SB;
   // Operands arrive in the tiled layout: a stage of a tile is one contiguous R-major block of
   // every panel (codes: rb_l bytes per row; B / W_L: 64 bytes = 32 groups per row; scales: SBL
-  // bytes per row), so every DMA instruction covers whole cache lines.
+  // bytes per row), so every DMA instruction covers whole cache lines.  A DMA address is the
+  // stage's panel base, the same for the whole wavefront (a buffer resource in scalar
+  // registers), plus the lane's fixed 32-bit offset inside the panel (rows < 2^24 of at most 128
+  // bytes): no per-stage vector address arithmetic.  With compensation both sides have 64-byte rows, so the code and
+  // the B / W_L panels share the offsets.
   const long code_panel = (long)R * rb_l;
   const long comp_panel = (long)R * 64;
   const long scale_panel = (long)R * C::SBL;
-  const uint8_t* src[C::NIMAX];
-  const uint8_t* srcC[COMP ? C::NIMAX : 1];
+  uint32_t voff[C::NIMAX];
 #pragma unroll
   for (int i = 0; i < C::NIMAX; ++i) {
     const int p = (C::NCW * i + cw) * 64 + lane;
@@ -211,17 +219,16 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const int r = p / cpr;
     const int pc = p % cpr;
     const int cc = rb_l == 64 ? swz<64>(r, pc) : swz<128>(r, pc);
-    const long gr = min(r0 + r, rmax);  // ragged edge: clamped rows are never stored
-    src[i] = gcodes + gr * rb_l + cc * 16;
-    if constexpr (COMP) srcC[i] = gcomp + gr * 64 + cc * 16;
+    const int gr = min(r0 + r, rmax);  // ragged edge: clamped rows are never stored
+    voff[i] = (uint32_t)gr * (uint32_t)rb_l + (uint32_t)(cc * 16);
   }
   // scale bytes: lane l of wave-instruction q covers row q*SRPI + l/SLPR, bytes 4*(l%SLPR)
-  const uint8_t* srcS[C::SCMAX];
+  uint32_t voffS[C::SCMAX];
 #pragma unroll
   for (int i = 0; i < C::SCMAX; ++i) {
     const int q = C::NCW * i + cw;
     const int r = q * C::SRPI + lane / C::SLPR;
-    srcS[i] = gscale + (long)min(r0 + r, rmax) * C::SBL + (lane % C::SLPR) * 4;
+    voffS[i] = (uint32_t)min(r0 + r, rmax) * C::SBL + (uint32_t)((lane % C::SLPR) * 4);
   }
 
   // Past the last stage the ring keeps issuing (reloads of the last stage into a free buffer), so
@@ -229,25 +236,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   auto issue = [&](int st_req, lds_u8* __restrict__ buf, bool may_comp) {
     const int st = min(st_req, nst - 1);
     const bool comp = COMP && may_comp && st < ncs;
-    if (comp) {
-      // compensation panel st; columns past KC (last panel) are loaded and zeroed at use
-      const long off = (long)st * comp_panel;
+    // compensation panel st (columns past KC in the last panel are loaded and zeroed at use),
+    // else code panel st - ncs
+    const auto rs = comp ? panel_rsrc(gcomp + (long)st * comp_panel, comp_panel)
+                         : panel_rsrc(gcodes + (long)(st - ncs) * code_panel, code_panel);
 #pragma unroll
-      for (int i = 0; i < C::NIMAX; ++i)
-        if (i < ni) dma16(srcC[COMP ? i : 0] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
-    } else {
-      const long off = (long)(st - ncs) * code_panel;
-#pragma unroll
-      for (int i = 0; i < C::NIMAX; ++i)
-        if (i < ni) dma16(src[i] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
-    }
+    for (int i = 0; i < C::NIMAX; ++i)
+      if (i < ni) dma16(rs, voff[i], buf + dst_rows + (C::NCW * i + cw) * 1024);
     // scales (also issued for compensation stages, from stage 0, so every stage has the same
     // number of loads per wave); with G=64 one scale panel serves two stages
     const int ks = comp ? 0 : st - ncs;
-    const long soff = (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel;
+    const auto ss = panel_rsrc(gscale + (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel, scale_panel);
 #pragma unroll
     for (int i = 0; i < C::SCMAX; ++i)
-      if (i < nsc) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);
+      if (i < nsc) dma4(ss, voffS[i], buf + dst_scale + (C::NCW * i + cw) * 256);
   };
 
   // Main-loop loads in two parts: the slots both DMA classes have (the first NIU code rows and
@@ -257,23 +259,23 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   constexpr int SCU = C::SCA < C::SCB ? C::SCA : C::SCB;
   auto issue_main_uniform = [&](int st_req, lds_u8* __restrict__ buf) {
     const int ks = min(st_req, nst - 1) - ncs;
-    const long off = (long)ks * code_panel;
+    const auto rs = panel_rsrc(gcodes + (long)ks * code_panel, code_panel);
 #pragma unroll
-    for (int i = 0; i < NIU; ++i) dma16(src[i] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
-    const long soff = (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel;
+    for (int i = 0; i < NIU; ++i) dma16(rs, voff[i], buf + dst_rows + (C::NCW * i + cw) * 1024);
+    const auto ss = panel_rsrc(gscale + (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel, scale_panel);
 #pragma unroll
-    for (int i = 0; i < SCU; ++i) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);
+    for (int i = 0; i < SCU; ++i) dma4(ss, voffS[i], buf + dst_scale + (C::NCW * i + cw) * 256);
   };
   auto issue_main_extra = [&](int st_req, lds_u8* __restrict__ buf) {
     const int ks = min(st_req, nst - 1) - ncs;
-    const long off = (long)ks * code_panel;
+    const auto rs = panel_rsrc(gcodes + (long)ks * code_panel, code_panel);
 #pragma unroll
     for (int i = NIU; i < C::NIMAX; ++i)
-      if (i < ni) dma16(src[i] + off, buf + dst_rows + (C::NCW * i + cw) * 1024);
-    const long soff = (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel;
+      if (i < ni) dma16(rs, voff[i], buf + dst_rows + (C::NCW * i + cw) * 1024);
+    const auto ss = panel_rsrc(gscale + (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel, scale_panel);
 #pragma unroll
     for (int i = SCU; i < C::SCMAX; ++i)
-      if (i < nsc) dma4(srcS[i] + soff, buf + dst_scale + (C::NCW * i + cw) * 256);
+      if (i < nsc) dma4(ss, voffS[i], buf + dst_scale + (C::NCW * i + cw) * 256);
   };
 
   v16f acc[C::TM][C::TN];
