@@ -195,6 +195,36 @@ osc_status osc_gemm_multi(const void* QX, const uint8_t* SX, const void* B, cons
 osc_status osc_build_table_multi(const void* Xcal, int R, int H, int G, double alpha, double rho, int m,
                                  int32_t* L, int32_t* hits, int32_t* events, void* stream);
 
+/*
+ * osc_swiglu_quant -- the input of a gated MLP's down-projection W2, quantized.
+ * Not an OSC step of its own: in a Qwen3-shaped block W2 reads h = silu(gate) *
+ * up, gate and up being the two halves of the up-projection's output, and §4
+ * switches that input to FP8 microscaling (or, by §2.3's clustering-density
+ * rule, it keeps the 4-bit OSC path).  This call fuses the glue into the
+ * quantization of osc_quant_act_multi, so h is never written to memory.
+ *   GU  [S][2F] bf16, device, read only: gate in columns [0, F), up in [F, 2F)
+ *       (the up-projection's Y with W1's rows packed before W3's).
+ *   h   per element, as binary32 operations: e = exp(-g), s = g / (1 + e)
+ *       (correctly rounded), h = bf16 round-to-nearest-even of s * u, where exp is
+ *       Cody and Waite's method: n = rint(x * log2 e), r = x - n ln2 (ln 2 split
+ *       into the head 45426/2^16 and a binary32 tail, two fused multiply-adds),
+ *       the degree-6 Taylor polynomial of e^r in Horner form with fused
+ *       multiply-adds, times 2^n; x > 88 gives +inf and x < -86 gives 0.
+ *   L, m, afmt, QX, SX, B  as osc_quant_act_multi with H = F: the tiled W2
+ *       activation operand (codes, scales and, with a table, B).
+ * Constraints: as osc_quant_act_multi with H = F, plus S * 2F < 2^34.
+ */
+osc_status osc_swiglu_quant(const void* GU, int S, int F, int G, const int32_t* L, int m, osc_fmt afmt,
+                            void* QX, uint8_t* SX, void* B, void* stream);
+
+/*
+ * osc_swiglu -- the same h written out: GU [S][2F] bf16 (device, read only) ->
+ * Hout [S][F] bf16 row-major (device, written), bit for bit the h that
+ * osc_swiglu_quant quantizes.  For calibrating the W2 table offline.
+ * Constraints: S >= 0, F > 0, F % 8 == 0, S < 2^24, S * 2F < 2^34.
+ */
+osc_status osc_swiglu(const void* GU, int S, int F, void* Hout, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* osc_status_str(osc_status s);
 

@@ -61,6 +61,16 @@ def lib():
         L.orc_build_table_multi.restype = i
         L.orc_threads.argtypes = []
         L.orc_threads.restype = i
+        L.orc_exp32.argtypes = [ctypes.c_float]
+        L.orc_exp32.restype = ctypes.c_float
+        L.orc_silu32.argtypes = [ctypes.c_float]
+        L.orc_silu32.restype = ctypes.c_float
+        L.orc_bf16_rne.argtypes = [ctypes.c_float]
+        L.orc_bf16_rne.restype = ctypes.c_uint16
+        L.orc_swiglu.argtypes = [P, i, i, P]
+        L.orc_swiglu.restype = None
+        L.orc_mean_density.argtypes = [P, P, i, i]
+        L.orc_mean_density.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -232,3 +242,47 @@ def osc_linear_multi(X, W, G: int, L, m: int):
     QX, SX, B = quant_act_multi(X, G, L, m)
     QW, SW, WL = pack_weights_multi(W, G, L, m)
     return gemm_comp(QX, SX, QW, SW, G, B, WL)
+
+
+# ------------------------------------------------ the MLP glue of a Qwen3-shaped block
+
+def exp32(x: float) -> float:
+    """The binary32 exponential the glue is defined with (Cody-Waite + Taylor, see osc_oracle.c)."""
+    return float(lib().orc_exp32(float(x)))
+
+
+def silu32(g: float) -> float:
+    return float(lib().orc_silu32(float(g)))
+
+
+def bf16_rne(f: float) -> int:
+    return int(lib().orc_bf16_rne(float(f)))
+
+
+def swiglu(GU: np.ndarray) -> np.ndarray:
+    """GU: uint16 bf16 bits [S, 2F] (gate | up) -> h = bf16(silu(gate) * up), uint16 [S, F]."""
+    GU = _c(GU, np.uint16)
+    S, F2 = GU.shape
+    assert F2 % 2 == 0
+    F = F2 // 2
+    Hh = np.zeros((S, F), np.uint16)
+    lib().orc_swiglu(_p(GU), S, F, _p(Hh))
+    return Hh
+
+
+def swiglu_quant(GU: np.ndarray, G: int, L=None, m: int = 1, fmt: int = MXFP4):
+    """The W2 input operand of the block: quantization (with extraction when L is given) of
+    h = swiglu(GU).  -> (QX, SX, B or None)."""
+    Hh = swiglu(GU)
+    if L is None:
+        return quant_act(Hh, G, None, fmt)
+    return quant_act_multi(Hh, G, L, m, fmt)
+
+
+def mean_density(hits: np.ndarray, events: np.ndarray) -> float:
+    """§2.2 clustering density C averaged over the groups that saw an outlier event."""
+    hits = _c(hits, np.int32)
+    events = _c(events, np.int32)
+    K = events.shape[0]
+    m = hits.size // K
+    return float(lib().orc_mean_density(_p(hits.reshape(K * m)), _p(events), K, m))

@@ -12,7 +12,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     src = os.path.join(HERE, "osc_oracle.c")
     tmp = LIB + ".tmp"
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", src, "-o", tmp, "-lm"]
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -395,3 +395,80 @@ int orc_build_table_multi(const uint16_t* Xcal, int R, int H, int G, double alph
   }
   return kept;
 }
+
+/* ------------------------------------------ the MLP glue between W1/W3 and W2 */
+
+/* Not an OSC step: in a Qwen3-shaped MLP block the down-projection W2 reads
+ * h = silu(gate) * up, gate = x W1^T and up = x W3^T (bf16 outputs of the
+ * up-projection GEMM).  So that the device can produce the same bits, h is
+ * defined as this sequence of binary32 operations (round to nearest even,
+ * subnormals kept, fused multiply-adds where written):
+ *   e = exp32(-g);  s = g / (1 + e);  h = bf16_rne(s * u).
+ * exp32(x), the method of Cody and Waite: n = rint(x * log2(e)) (one binary32
+ * product), r = x - n ln2 by two fused multiply-adds with ln2 split into a head
+ * of 16 significant bits (45426 / 2^16) and a binary32 tail, then e^r by its
+ * Taylor polynomial of degree 6 in Horner form (fused multiply-adds) and the
+ * exact scaling by 2^n.  x > 88 gives +inf (then s = -0 for g < -88) and
+ * x < -86 gives 0 (there 1 + e^x rounds to 1 in binary32 anyway), so every
+ * finite intermediate stays a normal number. */
+static const float kLog2e = 1.44269504088896341f;
+static const float kLn2Hi = 0.693145751953125f;      /* 45426 / 65536, exact */
+static const float kLn2Lo = 1.42860682030941723e-6f; /* ln 2 - kLn2Hi, rounded */
+
+float orc_exp32(float x) {
+  if (x > 88.0f) return INFINITY;
+  if (x < -86.0f) return 0.0f;
+  float n = rintf(x * kLog2e);
+  float r = fmaf(-n, kLn2Hi, x);
+  r = fmaf(-n, kLn2Lo, r);
+  float p = 1.0f / 720.0f;
+  p = fmaf(p, r, 1.0f / 120.0f);
+  p = fmaf(p, r, 1.0f / 24.0f);
+  p = fmaf(p, r, 1.0f / 6.0f);
+  p = fmaf(p, r, 0.5f);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)n);
+}
+
+float orc_silu32(float g) {
+  float e = orc_exp32(-g);
+  float d = 1.0f + e;
+  return g / d;
+}
+
+/* binary32 -> bf16 bits, round to nearest, ties to even (finite inputs). */
+uint16_t orc_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* GU: S x 2F bf16 bits, gate in columns [0, F), up in [F, 2F) -> Hout: S x F. */
+void orc_swiglu(const uint16_t* GU, int S, int F, uint16_t* Hout) {
+#pragma omp parallel for schedule(static)
+  for (int s = 0; s < S; ++s) {
+    for (int j = 0; j < F; ++j) {
+      float g = (float)orc_bf16_value(GU[(long)s * 2 * F + j]);
+      float u = (float)orc_bf16_value(GU[(long)s * 2 * F + F + j]);
+      float t = orc_silu32(g) * u;
+      Hout[(long)s * F + j] = orc_bf16_rne(t);
+    }
+  }
+}
+
+/* §2.2's clustering density of a built table: C_k = hits / events of the kept
+ * (first) entry of every group that saw an event, averaged over those groups;
+ * 0 when no group saw one.  hits: K x m (entry 0 used), events: K. */
+double orc_mean_density(const int32_t* hits, const int32_t* events, int K, int m) {
+  double sum = 0.0;
+  int n = 0;
+  for (int k = 0; k < K; ++k) {
+    if (events[k] > 0) {
+      sum += (double)hits[k * m] / (double)events[k];
+      ++n;
+    }
+  }
+  return n ? sum / n : 0.0;
+}

@@ -131,3 +131,16 @@ def assert_y_close(got: np.ndarray, ref: np.ndarray, rms=None, what=""):
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outputs outside tolerance; worst at {i}: "
                              f"got {got[i]!r} ref {ref[i]!r} bound {bound[i]!r}")
     return float((err / bound).max())
+
+
+def swiglu_quant(GU_dev: torch.Tensor, S: int, F: int, G: int, L, m: int, fmt: int):
+    """-> tiled device buffers (QX, SX, B or None) of h = silu(gate) * up, GU = [gate | up]."""
+    QX, SX, B = _tiled_outputs(S, F, G, fmt, L is not None, m)
+    osc.osc_swiglu_quant(GU_dev, S, F, G, L, m, fmt, QX, SX, B)
+    return QX, SX, B
+
+
+def swiglu(GU_dev: torch.Tensor, S: int, F: int) -> torch.Tensor:
+    Hh = poisoned((S, F), torch.int16)
+    osc.osc_swiglu(GU_dev, S, F, Hh)
+    return Hh

@@ -136,3 +136,30 @@ def test_multi_validation():
     b = lambda m=2: status("osc_build_table_multi", A, 1536, 256, 32, ctypes.c_double(5.0), ctypes.c_double(0.35),
                            m, A, A, A, None)
     assert b(m=0) == 2 and b(m=4) == 2
+
+
+def test_swiglu_quant_validation():
+    keep, lp = L8([-1] * 16)  # F=512, G=32: K=16
+    q = lambda GU=A, S=16, F=512, G=32, l=lp, m=1, f=1, QX=A, SX=A, B=A: status(
+        "osc_swiglu_quant", GU, S, F, G, l, m, f, QX, SX, B, None)
+    assert q(f=5) == 5                       # bad format
+    assert q(F=384) == 2                     # tiled layout: F % 256
+    assert q(G=8) == 2
+    assert q(m=0) == 2 and q(m=4) == 2
+    assert q(S=1 << 24) == 2                 # rows >= 2^24
+    assert q(S=(1 << 21) + 8, F=4096) == 2   # S * 2F >= 2^34 (S * F alone is below)
+    assert q(GU=None) == 1 and q(SX=None) == 1
+    assert q(B=None) == 1 and q(l=None) == 1  # table and B go together
+    assert q(GU=U) == 4 and q(QX=U) == 4
+    bad, bp = L8([0] * 15 + [32])
+    assert q(l=bp) == 3
+    assert q(S=0) == 0                       # nothing to do
+
+
+def test_swiglu_validation():
+    h = lambda GU=A, S=16, F=512, Ho=A: status("osc_swiglu", GU, S, F, Ho, None)
+    assert h(F=12) == 2 and h(F=0) == 2 and h(S=-1) == 2
+    assert h(S=1 << 24) == 2
+    assert h(GU=None) == 1 and h(Ho=None) == 1
+    assert h(GU=U) == 4 and h(Ho=U) == 4
+    assert h(S=0) == 0

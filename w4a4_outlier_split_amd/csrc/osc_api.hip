@@ -100,6 +100,35 @@ osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, o
   return osc_quant_act_multi(X, S, H, G, L, 1, afmt, QX, SX, B, stream);
 }
 
+osc_status osc_swiglu(const void* GU, int S, int F, void* Hout, void* stream) {
+  if (S < 0 || F <= 0 || F % 8 != 0) return OSC_E_SHAPE;
+  if (S >= (1 << 24) || (long long)S * (F / 4) > 0x7FFFFFFFLL) return OSC_E_SHAPE;
+  if (S == 0) return OSC_OK;
+  if (!GU || !Hout) return OSC_E_NULL;
+  if (!aligned16(GU) || !aligned16(Hout)) return OSC_E_ALIGN;
+  return from_hip(osc::launch_swiglu(GU, S, F, Hout, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_swiglu_quant(const void* GU, int S, int F, int G, const int32_t* L, int m, osc_fmt afmt, void* QX,
+                            uint8_t* SX, void* B, void* stream) {
+  if (afmt != OSC_MXFP4 && afmt != OSC_MXFP8) return OSC_E_FORMAT;
+  osc_status st = check_tiled(S, F, G);
+  if (st != OSC_OK) return st;
+  if ((long long)S * (F / 4) > 0x7FFFFFFFLL) return OSC_E_SHAPE;  // the input rows are 2F wide
+  if (!valid_m(m) || (F / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
+  if (S == 0) return OSC_OK;
+  if (!GU || !QX || !SX) return OSC_E_NULL;
+  if ((L == nullptr) != (B == nullptr)) return OSC_E_NULL;
+  if (!aligned16(GU) || !aligned16(QX) || !aligned16(SX) || (B && !aligned16(B))) return OSC_E_ALIGN;
+  osc::TableArg tab;
+  if (L) {
+    st = pack_table(L, F / G, m, G, &tab);
+    if (st != OSC_OK) return st;
+  }
+  return from_hip(osc::launch_quant(GU, S, F, G, m, L ? &tab : nullptr, L ? osc::kExtractZero : osc::kNoTable, afmt,
+                                    QX, SX, B, static_cast<hipStream_t>(stream), true));
+}
+
 osc_status osc_pack_weights_multi(const void* W, int N, int H, int G, const int32_t* L, int m, osc_fmt wfmt, void* QW,
                                   uint8_t* SW, void* WL, void* stream) {
   if (wfmt != OSC_MXFP4 && wfmt != OSC_MXFP8) return OSC_E_FORMAT;

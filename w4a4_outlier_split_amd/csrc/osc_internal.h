@@ -23,8 +23,14 @@ constexpr int kMaxChannels = 3;
 // entries per group, entry e of group k at v[k*m + e].
 //   mode kExtractZero: B(r, k*m+e) <- X[r][kG+L[k][e]], those slots are zeroed before scaling.
 //   mode kCopyOnly:    WL(r, k*m+e) <- W[r][kG+L[k][e]], nothing is zeroed.
+// glu: X holds rows of 2H bf16 (gate | up) and the row quantized is h = silu(gate) * up
+// (binary32, rounded to bf16), the input of a gated MLP's down-projection.
 hipError_t launch_quant(const void* X, int rows, int H, int G, int m, const TableArg* tab, int mode, osc_fmt fmt,
-                        void* Q, uint8_t* SC, void* side, hipStream_t st);
+                        void* Q, uint8_t* SC, void* side, hipStream_t st, bool glu = false);
+
+// h = silu(gate) * up (the same binary32 definition as the glu quantization), written as bf16:
+// GU rows of 2F bf16 -> Hout rows of F bf16.
+hipError_t launch_swiglu(const void* GU, int rows, int F, void* Hout, hipStream_t st);
 
 // Table slice with up to m entries per group: L and hits device int32[K*m], events int32[K].
 hipError_t launch_build_table(const void* Xcal, int R, int H, int G, int m, double alpha, double rho, int32_t* L,

@@ -113,9 +113,67 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, con
   }
 }
 
+// ------------------------------------------------------------------ MLP glue
+// In a Qwen3-shaped MLP block the down-projection reads h = silu(gate) * up, the two halves of
+// the up-projection's bf16 output (not an OSC step; the quantization of W2's input then follows
+// §3.2 / §4 as for any activation).  h is fixed as a sequence of binary32 operations so that it
+// is reproducible bit for bit: e = exp(-g), s = g / (1 + e) (correctly rounded division),
+// h = bf16 round-to-nearest-even of s * u.  exp by Cody and Waite's method: n = rint(x log2 e)
+// (one binary32 product), r = x - n ln2 with ln2 split into a 16-significant-bit head and a
+// binary32 tail (two fused multiply-adds), e^r by its degree-6 Taylor polynomial in Horner form
+// (fused multiply-adds), then the exact scaling by 2^n; x > 88 gives +inf and x < -86 gives 0,
+// so every finite intermediate is a normal number.
+__device__ __forceinline__ float glu_exp(float x) {
+#pragma clang fp contract(off)
+  if (x > 88.0f) return __builtin_inff();
+  if (x < -86.0f) return 0.0f;
+  const float n = __builtin_rintf(x * 1.44269504088896341f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, x);  // head: 45426 / 2^16, exact
+  r = __builtin_fmaf(-n, 1.42860682030941723e-6f, r);   // tail: ln 2 - head
+  float p = 1.0f / 720.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ uint32_t glu_one(uint32_t gbits, uint32_t ubits) {
+#pragma clang fp contract(off)
+  const float g = __builtin_bit_cast(float, gbits << 16);
+  const float u = __builtin_bit_cast(float, ubits << 16);
+  const float e = glu_exp(-g);
+  const float sv = g / (1.0f + e);
+  const uint32_t t = __builtin_bit_cast(uint32_t, sv * u);
+  return (t + 0x7FFFu + ((t >> 16) & 1u)) >> 16;  // round to nearest even (finite values)
+}
+
+// 8 bf16 of gate and the 8 of up at the same columns -> 8 bf16 of h
+__device__ __forceinline__ u4 glu_chunk(u4 g, u4 u) {
+  u4 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    h[i] = glu_one(g[i] & 0xFFFFu, u[i] & 0xFFFFu) | (glu_one(g[i] >> 16, u[i] >> 16) << 16);
+  return h;
+}
+
+// h written out (bf16, row-major S x F): the glue on its own, for calibrating the W2 table.
+__global__ __launch_bounds__(256) void k_swiglu(const u4* __restrict__ GU, int rows, int F, u4* __restrict__ Hout) {
+  const long chunks = (long)rows * (F >> 3);
+  for (long c = blockIdx.x * 256L + threadIdx.x; c < chunks; c += (long)gridDim.x * 256) {
+    const long r = c / (F >> 3);
+    const long q = c - r * (F >> 3);
+    const u4* row = GU + r * (F >> 2);
+    Hout[c] = glu_chunk(__builtin_nontemporal_load(row + q), __builtin_nontemporal_load(row + (F >> 3) + q));
+  }
+}
+
 constexpr int kRowsPerWave = 8;
 
-template <int G, int FMT, int MODE, int M>
+// GLU: X holds rows of 2H bf16 (gate | up) and the quantized row is h = glu(gate, up) of H.
+template <int G, int FMT, int MODE, int M, bool GLU = false>
 __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int rows, int H, TableArg tab,
                                                uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
                                                uint16_t* __restrict__ side) {
@@ -130,27 +188,50 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int row
   const int r0 = rb * kRowsPerWave + (lane >> 4);
   // rows past the end are skipped by whole 16-lane row segments, so a group's lanes agree
   constexpr int U = kRowsPerWave / 4;
-  u4 v[U];
+  u4 v[U], vu[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int r = r0 + 4 * u;
-    if (r < rows) v[u] = __builtin_nontemporal_load(X + (long)r * (H >> 3) + (col0 >> 3));
+    if (r < rows) {
+      if constexpr (GLU) {
+        const u4* row = X + (long)r * (H >> 2);
+        v[u] = __builtin_nontemporal_load(row + (col0 >> 3));
+        vu[u] = __builtin_nontemporal_load(row + ((H + col0) >> 3));
+      } else {
+        v[u] = __builtin_nontemporal_load(X + (long)r * (H >> 3) + (col0 >> 3));
+      }
+    }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int r = r0 + 4 * u;
-    if (r < rows) quant_chunk<G, FMT, MODE, M>(v[u], r, col0, rows, tab, Q, SC, side);
+    if (r < rows) quant_chunk<G, FMT, MODE, M>(GLU ? glu_chunk(v[u], vu[u]) : v[u], r, col0, rows, tab, Q, SC, side);
   }
 }
 
-template <int G, int FMT, int MODE>
+template <int G, int FMT, int MODE, bool GLU>
 hipError_t launch_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC, uint16_t* sd,
                     unsigned grid, hipStream_t st) {
   switch (m) {
-    case 1: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
-    case 2: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 2>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
-    default: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 3>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 1: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 1, GLU>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 2: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 2, GLU>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    default: hipLaunchKernelGGL((k_quant<G, FMT, MODE, 3, GLU>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
   }
+  return hipGetLastError();
+}
+
+template <int G, int FMT>
+hipError_t dispatch_glu(const void* X, int rows, int H, int m, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+                        void* side, hipStream_t st) {
+  const long waves = (long)((rows + kRowsPerWave - 1) / kRowsPerWave) * (H >> 7);
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const u4* x = static_cast<const u4*>(X);
+  uint8_t* q = static_cast<uint8_t*>(Q);
+  uint16_t* sd = static_cast<uint16_t*>(side);
+  static const TableArg empty = {};
+  const TableArg& t = tab ? *tab : empty;
+  if (mode == kExtractZero) return launch_m<G, FMT, kExtractZero, true>(x, rows, H, m, t, q, SC, sd, grid, st);
+  hipLaunchKernelGGL((k_quant<G, FMT, kNoTable, 1, true>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   return hipGetLastError();
 }
 
@@ -164,15 +245,19 @@ hipError_t dispatch_mode(const void* X, int rows, int H, int m, const TableArg* 
   uint16_t* sd = static_cast<uint16_t*>(side);
   static const TableArg empty = {};
   const TableArg& t = tab ? *tab : empty;
-  if (mode == kExtractZero) return launch_m<G, FMT, kExtractZero>(x, rows, H, m, t, q, SC, sd, grid, st);
-  if (mode == kCopyOnly) return launch_m<G, FMT, kCopyOnly>(x, rows, H, m, t, q, SC, sd, grid, st);
+  if (mode == kExtractZero) return launch_m<G, FMT, kExtractZero, false>(x, rows, H, m, t, q, SC, sd, grid, st);
+  if (mode == kCopyOnly) return launch_m<G, FMT, kCopyOnly, false>(x, rows, H, m, t, q, SC, sd, grid, st);
   hipLaunchKernelGGL((k_quant<G, FMT, kNoTable, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* tab, int mode, osc_fmt fmt,
+hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* tab, int mode, osc_fmt fmt, bool glu,
                         void* Q, uint8_t* SC, void* side, hipStream_t st) {
+  if (glu) {
+    if (fmt == OSC_MXFP4) return dispatch_glu<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
+    return dispatch_glu<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
+  }
   if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
   return dispatch_mode<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
 }
@@ -250,14 +335,25 @@ __global__ __launch_bounds__(256) void k_build_table(const uint16_t* __restrict_
 }  // namespace
 
 hipError_t launch_quant(const void* X, int rows, int H, int G, int m, const TableArg* tab, int mode, osc_fmt fmt,
-                        void* Q, uint8_t* SC, void* side, hipStream_t st) {
+                        void* Q, uint8_t* SC, void* side, hipStream_t st, bool glu) {
   const long nchunks = (long)rows * (H / 8);
   if (nchunks == 0) return hipSuccess;
+  if (glu && mode == kCopyOnly) return hipErrorInvalidValue;  // the glue feeds activations only
   switch (G) {
-    case 16: return dispatch_fmt<16>(X, rows, H, m, tab, mode, fmt, Q, SC, side, st);
-    case 32: return dispatch_fmt<32>(X, rows, H, m, tab, mode, fmt, Q, SC, side, st);
-    default: return dispatch_fmt<64>(X, rows, H, m, tab, mode, fmt, Q, SC, side, st);
+    case 16: return dispatch_fmt<16>(X, rows, H, m, tab, mode, fmt, glu, Q, SC, side, st);
+    case 32: return dispatch_fmt<32>(X, rows, H, m, tab, mode, fmt, glu, Q, SC, side, st);
+    default: return dispatch_fmt<64>(X, rows, H, m, tab, mode, fmt, glu, Q, SC, side, st);
   }
+}
+
+hipError_t launch_swiglu(const void* GU, int rows, int F, void* Hout, hipStream_t st) {
+  const long chunks = (long)rows * (F >> 3);
+  if (chunks == 0) return hipSuccess;
+  const long blocks = (chunks + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  hipLaunchKernelGGL(k_swiglu, dim3(grid), dim3(256), 0, st, static_cast<const u4*>(GU), rows, F,
+                     static_cast<u4*>(Hout));
+  return hipGetLastError();
 }
 
 hipError_t launch_build_table(const void* Xcal, int R, int H, int G, int m, double alpha, double rho, int32_t* L,
