@@ -344,6 +344,89 @@ def quality(torch, osc, w, variants, dev, nrows=32, seed=7):
     return {"metric": "||Y - X W^T|| / ||X W^T||", "rows_sampled": int(len(rows)), "errors": out}
 
 
+def run_block(torch, osc, dev, stream, steps, warmup, S=4096):
+    """The linear layers of a Qwen3-8B-shaped block through the block executor: QKV (N=6144),
+    Wo (4096), the MLP's stacked W1|W3 up-projection (N=24576) -> glue -> W2 (12288 -> 4096).
+    Each module's path follows the per-module rule on its own calibration rows (§2.3; W2's rows
+    are the glue output of the up-projection's calibration rows); the comparator runs every
+    module as W8A8 (MXFP8 activations and weights).  One step = the four layers back to back;
+    attention, norms and residual adds are not part of it (Wo's input is its own workload)."""
+    import numpy as np
+    import synth
+    from w4a4_outlier_split_amd import block as blk
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    H, F, G = 4096, 12288, 32
+    wq, wo, wu = synth.qkv(S=S), synth.attn_out(S=S), synth.ffn_up(S=S)
+    W2 = bf(synth.draw_w(H, F, 35))
+    Xq, Xo, Xu = bf(wq.X), bf(wo.X), bf(wu.X)
+    Wq, Wo, Wu = bf(wq.W), bf(wo.W), bf(wu.W)
+    cal = {n: blk.calibrate(torch, bf(w.calib), H, G, stream=stream) for n, w in (("qkv", wq), ("o", wo), ("up", wu))}
+    up_osc = blk.Linear(torch, Wu, 2 * F, H, G, cal["up"].path, cal["up"].L, stream=stream)
+    cal["down"] = blk.MLP(up_osc, blk.Linear(torch, W2, H, F, G, "fp8", stream=stream)).calibrate_down(
+        torch, bf(wu.calib), G, stream=stream)
+    flops = 2.0 * S * (H * 6144 + H * H + H * 2 * F + F * H)
+
+    def build(w8a8):
+        if w8a8:
+            mk = lambda W, N, K_in: blk.Linear(torch, W, N, K_in, G, "fp8", wfmt=osc.OSC_MXFP8, stream=stream)
+            return (mk(Wq, 6144, H), mk(Wo, H, H), blk.MLP(mk(Wu, 2 * F, H), mk(W2, H, F)))
+        mk = lambda W, N, K_in, c: blk.Linear(torch, W, N, K_in, G, c.path, c.L, stream=stream)
+        return (mk(Wq, 6144, H, cal["qkv"]), mk(Wo, H, H, cal["o"]),
+                blk.MLP(up_osc, mk(W2, H, F, cal["down"])))
+
+    def time_block(mods):
+        q, o, mlp = mods
+        aq, ao = q.act_buffers(S, dev), o.act_buffers(S, dev)
+        bufs = mlp.buffers(S, dev)
+        Yq = torch.empty((S, 6144), dtype=torch.bfloat16, device=dev)
+        Yo = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+        Ym = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+        calls = [lambda: q.forward(Xq, S, aq, Yq, stream=stream), lambda: o.forward(Xo, S, ao, Yo, stream=stream),
+                 lambda: mlp.forward(Xu, S, bufs, Ym, stream=stream)]
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                for c in calls:
+                    c()
+            ev = TimingEvents(2 + 4 * steps)
+            sh = stream.cuda_stream
+            gc.collect()
+            gc.disable()
+            torch.cuda.synchronize()
+            ev.record(0, sh)
+            for _ in range(steps):
+                for c in calls:
+                    c()
+            ev.record(1, sh)
+            for i in range(steps):  # per-module split
+                for j, c in enumerate(calls):
+                    ev.record(2 + 4 * i + j, sh)
+                    c()
+                ev.record(2 + 4 * i + 3, sh)
+            torch.cuda.synchronize()
+            gc.enable()
+        t = ev.ms(0, 1) / steps * 1e-3
+        split = [sum(ev.ms(2 + 4 * i + j, 2 + 4 * i + j + 1) for i in range(steps)) / steps * 1e3 for j in range(3)]
+        ev.close()
+        del aq, ao, bufs, Yq, Yo, Ym
+        return t, split
+
+    t_osc, split_osc = time_block(build(False))
+    t_w8, split_w8 = time_block(build(True))
+    row = {"workload": f"qwen3_block_linears_s{S}", "S": S,
+           "modules": {n: {"path": c.path, "density": c.density, "protected_groups": int((c.L >= 0).any(axis=1).sum())}
+                       for n, c in cal.items()},
+           "timing": "eager", "ms_per_step": t_osc * 1e3, "tflops": flops / t_osc / 1e12,
+           "split_us": dict(zip(("qkv", "o", "mlp"), split_osc)),
+           "w8a8_ms_per_step": t_w8 * 1e3, "w8a8_split_us": dict(zip(("qkv", "o", "mlp"), split_w8)),
+           "osc_speedup_vs_w8a8": t_w8 / t_osc, "flops_per_step": flops}
+    row["frac_of_mxfp4_peak"] = row["tflops"] / PEAK_TFLOPS["mxfp4"]
+    torch.cuda.empty_cache()
+    return row
+
+
 def cpu_baseline(w, L, target_s):
     """The oracle (quant + dual-path GEMM, fp64) on the first rows of the same workload,
     grown until the sample costs about target_s seconds of CPU time."""
@@ -446,6 +529,8 @@ def main():
             rows.append(run_row(torch, osc, "two_outlier_s2048_m1", wt, L1, 0, 0, dev, stream, 500, 1000))
             rows.append(run_row(torch, osc, "two_outlier_s2048_m2", wt, L2, 0, 0, dev, stream, 500, 1000, m=2))
             del wt
+        if want("block"):
+            rows.append(run_block(torch, osc, dev, stream, 50, 100))
         for S in (8192, 16):
             for G in (16, 32, 64):
                 n = f"gsweep_s{S}_g{G}"

@@ -99,6 +99,20 @@ def draw_x_laplace_group_spikes(S: int, H: int, plant: Plant, seed_z: int, seed_
     return to_bf16_bits(z)
 
 
+def draw_x_normal_group_spikes(S: int, H: int, plant: Plant, seed_z: int, seed_spike: int,
+                               spike: float = 20.0) -> np.ndarray:
+    """As draw_x_laplace_group_spikes with standard-normal base draws."""
+    z = np.random.default_rng(seed_z).standard_normal((S, H), dtype=np.float32)
+    _apply_plant(z, plant)
+    nblk = H // PLANT_BLOCK
+    free = np.setdiff1d(np.arange(nblk), plant.groups)
+    offs = np.random.default_rng(seed_spike).integers(0, PLANT_BLOCK, (S, free.size))
+    cols = free[None, :] * PLANT_BLOCK + offs
+    rows = np.repeat(np.arange(S)[:, None], free.size, axis=1)
+    z[rows, cols] *= spike
+    return to_bf16_bits(z)
+
+
 def draw_w(N: int, H: int, seed: int, std: float = 0.02) -> np.ndarray:
     w = np.random.default_rng(seed).standard_normal((N, H), dtype=np.float32) * np.float32(std)
     return to_bf16_bits(w)
@@ -175,6 +189,17 @@ def ffn_down(S: int = 4096) -> Workload:
     X = draw_x_laplace_group_spikes(S, H, plant, 32, 33)
     calib = draw_x_laplace_group_spikes(CALIB_ROWS, H, plant, 34, 34 + 100)
     return Workload(f"ffn_down_s{S}", S, H, N, G, X, 35, calib, None, plant)
+
+
+def attn_out(S: int = 4096) -> Workload:
+    """Qwen3-8B attention output projection Wo: H=N=4096; N(0,1); 45% of groups x U(40,100)
+    persistent, every other group one x20 spike per token at a random channel (Table 1 puts
+    this input's clustering density at 40-50 %)."""
+    H, N, G = 4096, 4096, 32
+    plant = draw_plant(61, H, 0.45, 40.0, 100.0)
+    X = draw_x_normal_group_spikes(S, H, plant, 62, 63)
+    calib = draw_x_normal_group_spikes(CALIB_ROWS, H, plant, 64, 64 + 100)
+    return Workload(f"attn_out_s{S}", S, H, N, G, X, 65, calib, None, plant)
 
 
 def group_sweep(S: int, G: int) -> Workload:
