@@ -190,8 +190,9 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
 def time_layer_graph(torch, osc, sets, reps, stream):
     """For launch-bound rows (a few microseconds of GPU work per kernel, less than the host
     needs to enqueue one): capture reps steps (rotating over the buffer sets) into one HIP
-    graph, and reps quantizations / reps GEMMs into two more, and time one replay of each.
-    Returns seconds per step, per quantization and per GEMM."""
+    graph, and reps quantizations / reps GEMMs into two more (and, for MXFP4 activations, reps
+    one-launch layers, osc_linear_decode, into a fourth), and time one replay of each.
+    Returns seconds per step, per quantization, per GEMM (and per fused layer, or None)."""
     def quant(l, s):
         P = l.ptr
         osc.osc_quant_act_multi(P["X"], l.S, l.H, l.G, l.L, l.m, l.afmt, P["QX"], P["SX"], P["B"], s)
@@ -205,6 +206,11 @@ def time_layer_graph(torch, osc, sets, reps, stream):
             osc.osc_gemm_fp8(P["QX"], P["SX"], P["QW"], P["SW"], l.wfmt, l.S, l.N, l.H, l.G, P["Y"],
                              osc.OSC_Y_BF16, s)
 
+    def fused(l, s):
+        P = l.ptr
+        osc.osc_linear_decode(P["X"], l.S, l.H, l.G, l.L, l.m, P["QW"], P["SW"], P["WL"], l.N, P["Y"],
+                              osc.OSC_Y_BF16, s)
+
     def capture(body):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
@@ -214,6 +220,8 @@ def time_layer_graph(torch, osc, sets, reps, stream):
         return g
 
     graphs = [capture(lambda l, cs: (quant(l, cs), gemm(l, cs))), capture(quant), capture(gemm)]
+    if sets[0].afmt == osc.OSC_MXFP4:
+        graphs.append(capture(fused))  # the one-launch decode layer
     out = []
     for g in graphs:
         g.replay()  # warm
@@ -223,6 +231,8 @@ def time_layer_graph(torch, osc, sets, reps, stream):
         torch.cuda.synchronize()
         out.append((time.perf_counter() - t0) / reps)
     del graphs
+    if len(out) == 3:
+        out.append(None)
     return tuple(out)
 
 
@@ -280,8 +290,9 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1)
     import numpy as np
     sets = make_sets(torch, osc, w, L, afmt, wfmt, dev, m)
     graphed = w.S <= 32  # decode shapes: kernels shorter than the host's enqueue time
+    tf = None
     if graphed:
-        wall, tq, tg = time_layer_graph(torch, osc, sets, steps, stream)
+        wall, tq, tg, tf = time_layer_graph(torch, osc, sets, steps, stream)
         host = wall
     else:
         wall, host, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
@@ -297,6 +308,13 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1)
            "gemm_tflops": flops / tg / 1e12,
            "quant_gbs": quant_bytes(w, afmt, comp) / tq / 1e9,
            "gemm_gbs": gemm_bytes(w, afmt, wfmt, comp) / tg / 1e9}
+    if tf is not None:
+        # the same layer as one launch (quantization fused into the decode GEMM)
+        row["fused_ms_per_step"] = tf * 1e3
+        K = w.H // w.G
+        fb = 2 * w.S * w.H + w.N * w.H / 2 + w.N * K + (2 * w.N * K * m if comp else 0) + 2 * w.S * w.N
+        row["fused_gbs"] = fb / tf / 1e9  # X read, packed weights read, Y written
+        row["fused_speedup"] = wall / tf
     peak = PEAK_TFLOPS["mxfp4"] if afmt == 0 else PEAK_TFLOPS["fp8"]
     row["gemm_frac_of_peak"] = row["gemm_tflops"] / peak
     row["frac_of_mxfp4_peak"] = row["tflops"] / PEAK_TFLOPS["mxfp4"]

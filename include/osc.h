@@ -196,6 +196,27 @@ osc_status osc_build_table_multi(const void* Xcal, int R, int H, int G, double a
                                  int32_t* L, int32_t* hits, int32_t* events, void* stream);
 
 /*
+ * osc_linear_decode -- the whole OSC layer in one launch for decode-sized batches
+ * (S <= 32 tokens): osc_quant_act_multi's extraction, zeroing, scale and E2M1
+ * encoding (§3.2) run inside the GEMM's workgroups, on X itself, and the result
+ * is bit for bit that of osc_quant_act_multi followed by osc_gemm_multi (same
+ * operands, same accumulation order); no Q_X / S_X / B buffers exist.
+ *   X   [S][H] bf16, device, row-major, read only.
+ *   L   host int32[K*m] table slice (as osc_quant_act_multi), or NULL for
+ *       direct MXFP4 (then WL must be NULL).
+ *   QW, SW, WL  the weights as osc_pack_weights_multi wrote them (MXFP4, same
+ *       L and m).
+ *   Y   [S][N], device, row-major, bf16 or fp32 (yt), written.
+ * Constraints: 0 <= S <= 32, N >= 0, G in {16, 32, 64}, H % 256 == 0,
+ * 1 <= m <= OSC_MAX_CHANNELS, m*K <= OSC_MAX_GROUPS, with a table (m*K) % 8 == 0,
+ * and the operands of one workgroup must fit its LDS: 16*H + 32*K +
+ * 2048*ceil(m*K/32) <= 160 KiB (H <= 8192 at G = 32 with m = 1); otherwise
+ * OSC_E_SHAPE and the two calls are the way.
+ */
+osc_status osc_linear_decode(const void* X, int S, int H, int G, const int32_t* L, int m, const void* QW,
+                             const uint8_t* SW, const void* WL, int N, void* Y, osc_ytype yt, void* stream);
+
+/*
  * osc_swiglu_quant -- the input of a gated MLP's down-projection W2, quantized.
  * Not an OSC step of its own: in a Qwen3-shaped block W2 reads h = silu(gate) *
  * up, gate and up being the two halves of the up-projection's output, and §4

@@ -144,3 +144,10 @@ def swiglu(GU_dev: torch.Tensor, S: int, F: int) -> torch.Tensor:
     Hh = poisoned((S, F), torch.int16)
     osc.osc_swiglu(GU_dev, S, F, Hh)
     return Hh
+
+
+def linear_decode(X_dev: torch.Tensor, S: int, H: int, G: int, L, m: int, QW, SW, WL, N: int,
+                  yt=osc.OSC_Y_F32) -> torch.Tensor:
+    Y = poisoned((S, N), torch.float32 if yt == osc.OSC_Y_F32 else torch.bfloat16)
+    osc.osc_linear_decode(X_dev, S, H, G, L, m, QW, SW, WL, N, Y, yt)
+    return Y

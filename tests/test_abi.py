@@ -163,3 +163,22 @@ def test_swiglu_validation():
     assert h(GU=None) == 1 and h(Ho=None) == 1
     assert h(GU=U) == 4 and h(Ho=U) == 4
     assert h(S=0) == 0
+
+
+def test_linear_decode_validation():
+    keep, lp = L8([-1] * 8)  # H=256, G=32: K=8
+    d = lambda X=A, S=16, H=256, G=32, l=lp, m=1, QW=A, SW=A, WL=A, N=128, Y=A, yt=0: status(
+        "osc_linear_decode", X, S, H, G, l, m, QW, SW, WL, N, Y, yt, None)
+    assert d(S=33) == 2                      # decode sizes only
+    assert d(S=-1) == 2 and d(N=-1) == 2
+    assert d(yt=2) == 5
+    assert d(H=384) == 2
+    assert d(m=4) == 2
+    assert d(H=256, G=64, l=L8([-1] * 4)[1]) == 2  # compensation columns 4: not a multiple of 8
+    assert d(H=16384, G=32, l=None, WL=None) == 2  # 256 KiB of quantized rows: more than LDS holds
+    assert d(WL=None) == 1 and d(l=None) == 1
+    assert d(X=None) == 1 and d(Y=None) == 1
+    assert d(X=U) == 4 and d(WL=U) == 4
+    bad, bp = L8([0, 1, 2, 3, 4, 5, 6, 40])
+    assert d(l=bp) == 3
+    assert d(S=0) == 0 and d(N=0) == 0

@@ -36,7 +36,7 @@ STATUS = {0: "OSC_OK", 1: "OSC_E_NULL", 2: "OSC_E_SHAPE", 3: "OSC_E_TABLE", 4: "
 
 EXPORTS = ("osc_pack_weights", "osc_quant_act", "osc_gemm", "osc_gemm_fp8", "osc_build_table",
            "osc_pack_weights_multi", "osc_quant_act_multi", "osc_gemm_multi", "osc_build_table_multi",
-           "osc_swiglu_quant", "osc_swiglu", "osc_status_str", "osc_last_device_error")
+           "osc_swiglu_quant", "osc_swiglu", "osc_linear_decode", "osc_status_str", "osc_last_device_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libosc.so is not built ({LIB_PATH}); run python w4a4_outlier_split_amd/build.py")
@@ -56,6 +56,7 @@ _lib.osc_gemm_multi.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, 
 _lib.osc_build_table_multi.argtypes = [_P, _I, _I, _I, _D, _D, _I, _P, _P, _P, _P]
 _lib.osc_swiglu_quant.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P]
 _lib.osc_swiglu.argtypes = [_P, _I, _I, _P, _P]
+_lib.osc_linear_decode.argtypes = [_P, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I, _P]
 for _f in EXPORTS[:-2]:
     getattr(_lib, _f).restype = _I
 _lib.osc_status_str.argtypes = [_I]
@@ -168,6 +169,13 @@ def osc_swiglu_quant(GU, S: int, F: int, G: int, L, m: int, afmt: int, QX, SX, B
     keep, lp = _table(L)
     _check(_lib.osc_swiglu_quant(_ptr(GU), S, F, G, lp, m, afmt, _ptr(QX), _ptr(SX), _ptr(B), _stream(stream)),
            "osc_swiglu_quant")
+
+
+def osc_linear_decode(X, S: int, H: int, G: int, L, m: int, QW, SW, WL, N: int, Y, yt: int, stream=None) -> None:
+    """S <= 32: quantization of X fused into the GEMM; Y equals quant_act_multi + gemm_multi."""
+    keep, lp = _table(L)
+    _check(_lib.osc_linear_decode(_ptr(X), S, H, G, lp, m, _ptr(QW), _ptr(SW), _ptr(WL), N, _ptr(Y), yt,
+                                  _stream(stream)), "osc_linear_decode")
 
 
 def osc_swiglu(GU, S: int, F: int, Hout, stream=None) -> None:

@@ -183,6 +183,29 @@ osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void
   return osc_gemm_multi(QX, SX, B, QW, SW, WL, S, N, H, G, 1, Y, yt, stream);
 }
 
+osc_status osc_linear_decode(const void* X, int S, int H, int G, const int32_t* L, int m, const void* QW,
+                             const uint8_t* SW, const void* WL, int N, void* Y, osc_ytype yt, void* stream) {
+  osc_status st = check_gemm(S, N, H, G, yt);
+  if (st != OSC_OK) return st;
+  if (S > osc::kDecodeRows) return OSC_E_SHAPE;
+  if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
+  if ((L == nullptr) != (WL == nullptr)) return OSC_E_NULL;
+  const int kc = L ? (H / G) * m : 0;
+  if (L && kc % 8 != 0) return OSC_E_SHAPE;
+  if (osc::fused_lds_bytes(H, G, kc) > 160 * 1024) return OSC_E_SHAPE;
+  if (S == 0 || N == 0) return OSC_OK;
+  if (!X || !QW || !SW || !Y) return OSC_E_NULL;
+  if (!aligned16(X) || !aligned16(QW) || !aligned16(SW) || !aligned16(Y) || (WL && !aligned16(WL)))
+    return OSC_E_ALIGN;
+  osc::TableArg tab;
+  if (L) {
+    st = pack_table(L, H / G, m, G, &tab);
+    if (st != OSC_OK) return st;
+  }
+  osc::FusedArgs a{X, &tab, m, QW, SW, WL, Y, S, N, H, G, kc, yt};
+  return from_hip(osc::launch_linear_dec(a, static_cast<hipStream_t>(stream)));
+}
+
 osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, const uint8_t* SW, osc_fmt wfmt, int S,
                         int N, int H, int G, void* Y, osc_ytype yt, void* stream) {
   if (wfmt != OSC_MXFP4 && wfmt != OSC_MXFP8) return OSC_E_FORMAT;

@@ -56,4 +56,22 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 constexpr int kDecodeRows = 32;
 hipError_t launch_gemm_dec(const GemmArgs& a, hipStream_t st);
 
+// S <= 32 rows with the activation quantization fused into the skinny-S GEMM (MXFP4 both sides):
+// X [S][H] bf16 row-major, the table (or none: WL == nullptr), the packed weights.
+struct FusedArgs {
+  const void* X;
+  const TableArg* tab;
+  int m;
+  const void* QW;
+  const uint8_t* SW;
+  const void* WL;
+  void* Y;
+  int S, N, H, G;
+  int kc;  // compensation columns (m*K), 0 without compensation
+  osc_ytype yt;
+};
+// LDS bytes the fused kernel needs for this shape (the limit is 160 KiB per workgroup).
+long fused_lds_bytes(int H, int G, int kc);
+hipError_t launch_linear_dec(const FusedArgs& a, hipStream_t st);
+
 }  // namespace osc
