@@ -445,6 +445,56 @@ def run_block(torch, osc, dev, stream, steps, warmup, S=4096):
     return row
 
 
+def block_quality(torch, osc, dev, nrows=16, seed=7):
+    """The gated MLP of the block (FFN-up workload -> W1|W3 -> glue -> W2) on sampled token rows:
+    relative error of the output against the exact chain (fp64 on the host: x W13^T, silu(gate) *
+    up, h W2^T), for the per-module rule (OSC up, FP8 W2), OSC on both, MXFP4 without tables and
+    W8A8.  Context for §4's fallback argument, not a gate."""
+    import numpy as np
+    import synth
+    from w4a4_outlier_split_amd import block as blk
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    H, F, G = 4096, 12288, 32
+    wu = synth.ffn_up(S=4096)
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(wu.S, size=nrows, replace=False))
+    X = wu.X[rows]
+    W13 = wu.W
+    W2 = synth.draw_w(H, F, 35)
+    f64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    y1 = f64(X) @ f64(W13).T
+    g, u = y1[:, :F], y1[:, F:]
+    ref = (g / (1.0 + np.exp(-g)) * u) @ f64(W2).T
+    nref = float(np.linalg.norm(ref))
+    W13d, W2d, Xd = bf(W13), bf(W2), bf(X)
+    c_up = blk.calibrate(torch, bf(wu.calib), H, G)
+    probe = blk.MLP(blk.Linear(torch, W13d, 2 * F, H, G, "osc", c_up.L), blk.Linear(torch, W2d, H, F, G, "fp8"))
+    c_dn = probe.calibrate_down(torch, bf(wu.calib), G)
+    variants = {
+        "rule (OSC up, FP8 W2)": (("osc", c_up.L, osc.OSC_MXFP4), ("fp8", None, osc.OSC_MXFP4)),
+        "OSC both": (("osc", c_up.L, osc.OSC_MXFP4), ("osc", c_dn.L, osc.OSC_MXFP4)),
+        "MXFP4 direct": (("osc", -np.ones_like(c_up.L), osc.OSC_MXFP4), ("osc", -np.ones_like(c_dn.L), osc.OSC_MXFP4)),
+        "W8A8": (("fp8", None, osc.OSC_MXFP8), ("fp8", None, osc.OSC_MXFP8)),
+    }
+    out = {}
+    for name, ((pu, Lu, wfu), (pd, Ld, wfd)) in variants.items():
+        up = blk.Linear(torch, W13d, 2 * F, H, G, pu, Lu, wfmt=wfu)
+        dn = blk.Linear(torch, W2d, H, F, G, pd, Ld, wfmt=wfd)
+        mlp = blk.MLP(up, dn)
+        bufs = mlp.buffers(nrows, dev)
+        Y = torch.empty((nrows, H), dtype=torch.float32, device=dev)
+        mlp.forward(Xd, nrows, bufs, Y, osc.OSC_Y_F32)
+        torch.cuda.synchronize()
+        out[name] = float(np.linalg.norm(Y.double().cpu().numpy() - ref)) / nref
+        del up, dn, mlp, bufs, Y
+    torch.cuda.empty_cache()
+    return {"metric": "||Y - Y_exact|| / ||Y_exact|| of the MLP output", "rows_sampled": nrows,
+            "w2_density": c_dn.density, "errors": out}
+
+
 def cpu_baseline(w, L, target_s):
     """The oracle (quant + dual-path GEMM, fp64) on the first rows of the same workload,
     grown until the sample costs about target_s seconds of CPU time."""
@@ -577,6 +627,7 @@ def main():
         qual["ffn_down_s4096"] = quality(torch, osc, wdn, [("w8a4_fp8", None, 1, 0), ("forced_osc", Ld, 0, 0),
                                                            ("mxfp4_direct", None, 0, 0)], dev, nrows=16)
         del wdn
+        qual["block_mlp_s4096"] = block_quality(torch, osc, dev)
 
     if head is None:
         print(json.dumps({"rows": rows, "quality": qual}))
