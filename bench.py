@@ -365,8 +365,9 @@ def quality(torch, osc, w, variants, dev, nrows=32, seed=7):
 def run_block(torch, osc, dev, stream, steps, warmup, S=4096):
     """The linear layers of a Qwen3-8B-shaped block through the block executor: QKV (N=6144),
     Wo (4096), the MLP's stacked W1|W3 up-projection (N=24576) -> glue -> W2 (12288 -> 4096).
-    Each module's path follows the per-module rule on its own calibration rows (§2.3; W2's rows
-    are the glue output of the up-projection's calibration rows); the comparator runs every
+    Each module's group size follows the two-channel rule (block.py; §6's dynamic-G direction) and
+    its path the per-module density rule (§2.3), both on its own calibration rows (W2's rows are
+    the glue output of the up-projection's calibration rows); the comparator runs every
     module as W8A8 (MXFP8 activations and weights).  One step = the four layers back to back;
     attention, norms and residual adds are not part of it (Wo's input is its own workload)."""
     import numpy as np
@@ -381,19 +382,31 @@ def run_block(torch, osc, dev, stream, steps, warmup, S=4096):
     W2 = bf(synth.draw_w(H, F, 35))
     Xq, Xo, Xu = bf(wq.X), bf(wo.X), bf(wu.X)
     Wq, Wo, Wu = bf(wq.W), bf(wo.W), bf(wu.W)
-    cal = {n: blk.calibrate(torch, bf(w.calib), H, G, stream=stream) for n, w in (("qkv", wq), ("o", wo), ("up", wu))}
-    up_osc = blk.Linear(torch, Wu, 2 * F, H, G, cal["up"].path, cal["up"].L, stream=stream)
-    cal["down"] = blk.MLP(up_osc, blk.Linear(torch, W2, H, F, G, "fp8", stream=stream)).calibrate_down(
-        torch, bf(wu.calib), G, stream=stream)
+    # per module: group size by the two-channel rule (§6 direction), then the path by the density
+    # rule (§2.3) at that group size
+    gsz, shares, cal = {}, {}, {}
+
+    def plan(n, xc, width):
+        gsz[n], shares[n] = blk.calibrate_group_size(torch, xc, width, stream=stream)
+        cal[n] = blk.calibrate(torch, xc, width, gsz[n], stream=stream)
+        if cal[n].path == "fp8" and gsz[n] == 16:  # the FP8 path's scales cover 32 or 64 channels
+            gsz[n] = 32
+            cal[n] = blk.calibrate(torch, xc, width, 32, stream=stream)
+
+    for n, w in (("qkv", wq), ("o", wo), ("up", wu)):
+        plan(n, bf(w.calib), H)
+    up_osc = blk.Linear(torch, Wu, 2 * F, H, gsz["up"], cal["up"].path, cal["up"].L, stream=stream)
+    hc = blk.MLP(up_osc, blk.Linear(torch, W2, H, F, G, "fp8", stream=stream)).glue_rows(torch, bf(wu.calib), stream)
+    plan("down", hc, F)
+    del hc
     flops = 2.0 * S * (H * 6144 + H * H + H * 2 * F + F * H)
 
     def build(w8a8):
         if w8a8:
             mk = lambda W, N, K_in: blk.Linear(torch, W, N, K_in, G, "fp8", wfmt=osc.OSC_MXFP8, stream=stream)
             return (mk(Wq, 6144, H), mk(Wo, H, H), blk.MLP(mk(Wu, 2 * F, H), mk(W2, H, F)))
-        mk = lambda W, N, K_in, c: blk.Linear(torch, W, N, K_in, G, c.path, c.L, stream=stream)
-        return (mk(Wq, 6144, H, cal["qkv"]), mk(Wo, H, H, cal["o"]),
-                blk.MLP(up_osc, mk(W2, H, F, cal["down"])))
+        mk = lambda W, N, K_in, n: blk.Linear(torch, W, N, K_in, gsz[n], cal[n].path, cal[n].L, stream=stream)
+        return (mk(Wq, 6144, H, "qkv"), mk(Wo, H, H, "o"), blk.MLP(up_osc, mk(W2, H, F, "down")))
 
     def time_block(mods):
         q, o, mlp = mods
@@ -434,8 +447,8 @@ def run_block(torch, osc, dev, stream, steps, warmup, S=4096):
     t_osc, split_osc = time_block(build(False))
     t_w8, split_w8 = time_block(build(True))
     row = {"workload": f"qwen3_block_linears_s{S}", "S": S,
-           "modules": {n: {"path": c.path, "density": c.density, "protected_groups": int((c.L >= 0).any(axis=1).sum())}
-                       for n, c in cal.items()},
+           "modules": {n: {"G": gsz[n], "two_channel_share": shares[n], "path": c.path, "density": c.density,
+                           "protected_groups": int((c.L >= 0).any(axis=1).sum())} for n, c in cal.items()},
            "timing": "eager", "ms_per_step": t_osc * 1e3, "tflops": flops / t_osc / 1e12,
            "split_us": dict(zip(("qkv", "o", "mlp"), split_osc)),
            "w8a8_ms_per_step": t_w8 * 1e3, "w8a8_split_us": dict(zip(("qkv", "o", "mlp"), split_w8)),
@@ -598,7 +611,7 @@ def main():
             rows.append(run_row(torch, osc, "two_outlier_s2048_m2", wt, L2, 0, 0, dev, stream, 500, 1000, m=2))
             del wt
         if want("block"):
-            rows.append(run_block(torch, osc, dev, stream, 50, 100))
+            rows.append(run_block(torch, osc, dev, stream, 100, 400))
         for S in (8192, 16):
             for G in (16, 32, 64):
                 n = f"gsweep_s{S}_g{G}"

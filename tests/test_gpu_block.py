@@ -85,3 +85,12 @@ def test_mlp_through_the_executor(down_path):
         qw, sw, _ = oracle.pack_weights(W2, G, None)
         ref = oracle.gemm(rq, rs, qw, sw, G, afmt=oracle.MXFP8, wfmt=oracle.MXFP4)
     assert_y_close(host_y(Y), ref, what=f"W2 ({down_path}) through the executor")
+
+
+@pytest.mark.parametrize("gen", ["qkv", "attn_out"])
+def test_group_size_rule_matches_the_oracle(gen):
+    w = getattr(synth, gen)(S=16)
+    G, shares = blk.calibrate_group_size(torch, dev_bf16(w.calib), w.H)
+    ref = {g: blk.two_share(oracle.build_table_multi(w.calib, g, 2)[0]) for g in (64, 32, 16)}
+    assert shares == pytest.approx(ref, abs=0)
+    assert G == blk.choose_group_size(ref)

@@ -20,7 +20,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import (OSC_MXFP4, OSC_MXFP8, OSC_Y_BF16, code_bytes, osc_build_table_multi, osc_gemm_fp8,
+from . import (OSC_MAX_GROUPS, OSC_MXFP4, OSC_MXFP8, OSC_Y_BF16, code_bytes, osc_build_table_multi, osc_gemm_fp8,
                osc_gemm_multi, osc_pack_weights_multi, osc_quant_act_multi, osc_swiglu, osc_swiglu_quant,
                scale_bytes, side_elems)
 
@@ -63,6 +63,46 @@ def calibrate(torch, Xcal, H: int, G: int = 32, m: int = 1, stream=None,
     eh = ev.cpu().numpy()
     c = mean_density(hh, eh)
     return Calibration(Lh, hh, eh, c, "osc" if c >= threshold else "fp8")
+
+
+# ------------------------------------------------------------------ per-layer group size (§6)
+# §6 names "dynamic group size" (G adapted per layer among 16 / 32 / 64) as a direction only.
+# Reading: a larger G is faster (Table 2), but a group can protect only the channels its table
+# entries list; G is too large for a layer when its groups often hold two persistent outlier
+# channels.  For each candidate G, fastest first, the table is built with two entries per group on
+# the layer's calibration rows; two_share = the share of the protected groups whose second entry
+# is also kept (a second consistent channel).  The layer takes the largest G whose two_share is at
+# most `tolerance`, else the G with the smallest two_share (larger G on ties).
+
+GROUP_SIZES = (64, 32, 16)
+TWO_SHARE_TOLERANCE = 0.10
+
+
+def two_share(L2: np.ndarray) -> float:
+    """L2: int[K, 2] table slice built with two entries per group."""
+    L2 = np.asarray(L2).reshape(-1, 2)
+    protected = L2[:, 0] >= 0
+    if not protected.any():
+        return 0.0
+    return float(np.mean(L2[protected, 1] >= 0))
+
+
+def choose_group_size(shares: dict, tolerance: float = TWO_SHARE_TOLERANCE) -> int:
+    """shares: {G: two_share}.  The rule above."""
+    for G in sorted(shares, reverse=True):
+        if shares[G] <= tolerance:
+            return G
+    return min(sorted(shares, reverse=True), key=lambda g: shares[g])
+
+
+def calibrate_group_size(torch, Xcal, H: int, sizes=GROUP_SIZES, tolerance: float = TWO_SHARE_TOLERANCE,
+                         stream=None):
+    """-> (chosen G, {G: two_share}) for one layer's calibration rows Xcal [R, H] (device bf16)."""
+    shares = {}
+    for G in sizes:
+        if H % 256 == 0 and H // G * 2 <= OSC_MAX_GROUPS:
+            shares[G] = two_share(calibrate(torch, Xcal, H, G, m=2, stream=stream).L)
+    return choose_group_size(shares, tolerance), shares
 
 
 class Linear:
@@ -136,9 +176,8 @@ class MLP:
         osc_swiglu_quant(bufs["gu"], S, self.F, d.G, d.L, d.m, d.afmt, QX, SX, B, stream)
         d.gemm(bufs["h"], S, Y, yt, stream)
 
-    def calibrate_down(self, torch, Xcal, G: int = 32, m: int = 1, stream=None,
-                       threshold: float = DENSITY_THRESHOLD) -> Calibration:
-        """The W2 input's calibration rows: Xcal pushed through the up-projection and the glue."""
+    def glue_rows(self, torch, Xcal, stream=None):
+        """W2's calibration rows: Xcal [R, H] pushed through the up-projection and the glue."""
         R = Xcal.shape[0]
         dev = Xcal.device
         act = self.up.act_buffers(R, dev)
@@ -146,4 +185,9 @@ class MLP:
         self.up.forward(Xcal, R, act, gu, OSC_Y_BF16, stream)
         h = torch.empty((R, self.F), dtype=torch.bfloat16, device=dev)
         osc_swiglu(gu, R, self.F, h, stream)
-        return calibrate(torch, h, self.F, G, m, stream, threshold)
+        return h
+
+    def calibrate_down(self, torch, Xcal, G: int = 32, m: int = 1, stream=None,
+                       threshold: float = DENSITY_THRESHOLD) -> Calibration:
+        """The per-module rule on W2's calibration rows (glue_rows)."""
+        return calibrate(torch, self.glue_rows(torch, Xcal, stream), self.F, G, m, stream, threshold)
