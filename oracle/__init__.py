@@ -19,6 +19,7 @@ from . import build as _build
 
 MXFP4 = 0
 MXFP8 = 1
+FP6P = 2  # E3M2 codes, one E8M0 scale per pair of 16-groups
 
 _lib = None
 
@@ -71,6 +72,14 @@ def lib():
         L.orc_swiglu.restype = None
         L.orc_mean_density.argtypes = [P, P, i, i]
         L.orc_mean_density.restype = ctypes.c_double
+        L.orc_e3m2_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e3m2_decode.restype = ctypes.c_double
+        L.orc_e3m2_encode.argtypes = [ctypes.c_double]
+        L.orc_e3m2_encode.restype = ctypes.c_uint8
+        L.orc_quant_act_fp6p.argtypes = [P, i, i, P, i, P, P, P]
+        L.orc_quant_act_fp6p.restype = None
+        L.orc_pack_weights_fp6p.argtypes = [P, i, i, P, i, P, P, P]
+        L.orc_pack_weights_fp6p.restype = None
         _lib = L
     return _lib
 
@@ -117,7 +126,7 @@ def scale_exp(amax: float, fmt: int) -> int:
 # ------------------------------------------------------------ array entry points
 
 def code_bytes_per_row(H: int, fmt: int) -> int:
-    return H // 2 if fmt == MXFP4 else H
+    return H // 2 if fmt == MXFP4 else H if fmt == MXFP8 else 3 * H // 4
 
 
 def quant_act(X: np.ndarray, G: int, L: Optional[np.ndarray], fmt: int = MXFP4
@@ -286,3 +295,60 @@ def mean_density(hits: np.ndarray, events: np.ndarray) -> float:
     K = events.shape[0]
     m = hits.size // K
     return float(lib().orc_mean_density(_p(hits.reshape(K * m)), _p(events), K, m))
+
+
+# ------------------------------------------------ G = 16 pairs in E3M2 (fast G = 16)
+
+def e3m2_decode(code: int) -> float:
+    return float(lib().orc_e3m2_decode(code))
+
+
+def e3m2_encode(v: float) -> int:
+    return int(lib().orc_e3m2_encode(float(v)))
+
+
+def get_code6(Q6: np.ndarray, k: int) -> np.ndarray:
+    """6-bit code k of every row of a packed E3M2 buffer (element k at bits [6k, 6k+6))."""
+    bit = 6 * k
+    b, sh = bit >> 3, bit & 7
+    w = Q6[:, b].astype(np.uint32) >> sh
+    if sh > 2:
+        w |= Q6[:, b + 1].astype(np.uint32) << (8 - sh)
+    return (w & 0x3F).astype(np.uint8)
+
+
+def quant_act_fp6p(X: np.ndarray, L=None, m: int = 1):
+    """G = 16 with extraction, re-encoded as E3M2 pairs -> (Q6 uint8[S, 3H/4], S32 uint8[S, H/32],
+    B uint16[S, H/16*m] or None)."""
+    X = _c(X, np.uint16)
+    S, H = X.shape
+    Q6 = np.zeros((S, 3 * H // 4), np.uint8)
+    S32 = np.zeros((S, H // 32), np.uint8)
+    B = None if L is None else np.zeros((S, H // 16 * m), np.uint16)
+    Lc = None if L is None else _c(L, np.int32).reshape(-1)
+    lib().orc_quant_act_fp6p(_p(X), S, H, _p(Lc), m, _p(Q6), _p(S32), _p(B))
+    return Q6, S32, B
+
+
+def pack_weights_fp6p(W: np.ndarray, L=None, m: int = 1):
+    W = _c(W, np.uint16)
+    N, H = W.shape
+    Q6 = np.zeros((N, 3 * H // 4), np.uint8)
+    S32 = np.zeros((N, H // 32), np.uint8)
+    WL = None if L is None else np.zeros((N, H // 16 * m), np.uint16)
+    Lc = None if L is None else _c(L, np.int32).reshape(-1)
+    lib().orc_pack_weights_fp6p(_p(W), N, H, _p(Lc), m, _p(Q6), _p(S32), _p(WL))
+    return Q6, S32, WL
+
+
+def gemm_fp6p(Q6X, S32X, Q6W, S32W, B=None, WL=None) -> np.ndarray:
+    """Y of E3M2-pair operands (scale blocks of 32) plus the compensation B WL^T (any width)."""
+    Q6X, S32X, Q6W, S32W = (_c(a, np.uint8) for a in (Q6X, S32X, Q6W, S32W))
+    S, N = Q6X.shape[0], Q6W.shape[0]
+    H = S32X.shape[1] * 32
+    Bc = None if B is None else _c(B, np.uint16)
+    WLc = None if WL is None else _c(WL, np.uint16)
+    KC = 0 if Bc is None else Bc.shape[1]
+    Y = np.zeros((S, N), np.float64)
+    lib().orc_gemm_comp(_p(Q6X), _p(S32X), FP6P, _p(Bc), _p(Q6W), _p(S32W), FP6P, _p(WLc), S, N, H, 32, KC, _p(Y))
+    return Y

@@ -43,6 +43,7 @@
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_MXFP4 0
@@ -115,12 +116,18 @@ int orc_scale_exp(double amax, int fmt) {
   return e;
 }
 
+double orc_e3m2_decode(uint8_t code);
+static uint8_t get_code6(const uint8_t* row, long k);
+
+/* bytes per row of element codes */
+static long code_stride(int H, int fmt) { return fmt == ORC_MXFP4 ? H / 2 : fmt == ORC_MXFP8 ? H : 3L * H / 4; }
+
 static uint8_t encode_elem(double v, int fmt) {
   return fmt == ORC_MXFP4 ? orc_e2m1_encode(v) : orc_e4m3_encode(v);
 }
 
 static double decode_elem(uint8_t c, int fmt) {
-  return fmt == ORC_MXFP4 ? orc_e2m1_decode(c) : orc_e4m3_decode(c);
+  return fmt == ORC_MXFP4 ? orc_e2m1_decode(c) : fmt == ORC_MXFP8 ? orc_e4m3_decode(c) : orc_e3m2_decode(c);
 }
 
 /* Store element code i of a row: MXFP4 packs two per byte, element 2i in the
@@ -137,6 +144,7 @@ static void put_code(uint8_t* row, int i, uint8_t code, int fmt) {
 
 static uint8_t get_code(const uint8_t* row, int i, int fmt) {
   if (fmt == ORC_MXFP8) return row[i];
+  if (fmt == 2) return get_code6(row, i);
   return (i % 2 == 0) ? (row[i / 2] & 0x0F) : (row[i / 2] >> 4);
 }
 
@@ -206,13 +214,14 @@ void orc_pack_weights(const uint16_t* W, int N, int H, int G, const int32_t* L, 
  *                         + sum_k B[s, k] * WL[n, k]
  * in fp64 (every product of two decoded codes, and of two bf16 values, is
  * exact in fp64).  B / WL may be NULL: no compensation path (plain MX GEMM,
- * and the FP8 fallback of §4).  afmt / wfmt: element format of each side. */
+ * and the FP8 fallback of §4).  afmt / wfmt: element format of each side
+ * (E3M2 pairs: fmt 2 with G = 32, one scale per 32 elements). */
 void orc_gemm_comp(const uint8_t* QX, const uint8_t* SX, int afmt, const uint16_t* B,
                    const uint8_t* QW, const uint8_t* SW, int wfmt, const uint16_t* WL,
                    int S, int N, int H, int G, int KC, double* Y) {
   int K = H / G;
-  long xstride = (afmt == ORC_MXFP4) ? H / 2 : H;
-  long wstride = (wfmt == ORC_MXFP4) ? H / 2 : H;
+  long xstride = code_stride(H, afmt);
+  long wstride = code_stride(H, wfmt);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int s = 0; s < S; ++s) {
     for (int n = 0; n < N; ++n) {
@@ -471,4 +480,96 @@ double orc_mean_density(const int32_t* hits, const int32_t* events, int K, int m
     }
   }
   return n ? sum / n : 0.0;
+}
+
+/* ------------------------------ G = 16 pairs re-encoded in E3M2 (fast G = 16) */
+
+/* §3.3 Table 2 measures G = 16, but a scaled matrix instruction of the MI355X
+ * takes one E8M0 scale per 32 elements.  Reading: the two 16-groups 2b and
+ * 2b+1 of a row, quantized exactly as MXFP4 at G = 16 (E2M1 codes c at their
+ * own E8M0 codes s_0, s_1, after the extraction of §3.2), are carried by one
+ * scale code E = max(s_0, s_1) - 2 (at least 0) and 32 E3M2 codes of the same
+ * values: code = nearest E3M2 value (ties to the even code) of
+ * dq(c) * 2^(s_i - E).  The E3M2 grid (OCP MX FP6 E3M2: bias 3, subnormals
+ * m/16, largest 28) holds every such value exactly while s_hi - s_lo <= 5; a
+ * pair whose groups differ by more rounds the smaller group's values.  Codes
+ * are packed 6 bits per element, element k at bits [6k, 6k+6) of the row
+ * (little-endian bytes).  fmt ORC_FP6P marks these operands: one E8M0 byte per
+ * 32 elements. */
+#define ORC_FP6P 2
+
+/* E3M2: sign bit 5, exponent bits 4..2 (bias 3), mantissa bits 1..0. */
+double orc_e3m2_decode(uint8_t code) {
+  int s = (code >> 5) & 1, e = (code >> 2) & 7, m = code & 3;
+  double mag = (e == 0) ? m / 16.0 : ldexp(1.0 + m / 4.0, e - 3);
+  return s ? -mag : mag;
+}
+
+uint8_t orc_e3m2_encode(double v) { return nearest_code(v, 32, orc_e3m2_decode, 5); }
+
+static void put_code6(uint8_t* row, long k, uint8_t code) {
+  long bit = 6 * k;
+  long byte = bit >> 3;
+  int sh = (int)(bit & 7);
+  row[byte] = (uint8_t)((row[byte] & ~(0x3F << sh)) | (code << sh));
+  if (sh > 2) row[byte + 1] = (uint8_t)((row[byte + 1] & ~(0x3F >> (8 - sh))) | (code >> (8 - sh)));
+}
+
+static uint8_t get_code6(const uint8_t* row, long k) {
+  long bit = 6 * k;
+  long byte = bit >> 3;
+  int sh = (int)(bit & 7);
+  unsigned w = row[byte] >> sh;
+  if (sh > 2) w |= (unsigned)row[byte + 1] << (8 - sh);
+  return (uint8_t)(w & 0x3F);
+}
+
+/* Re-encode rows of a G = 16 MXFP4 quantization (Q4: rows x H/2, S16: rows x H/16)
+ * into the E3M2 pairs (Q6: rows x 3H/4, S32: rows x H/32). */
+static void reencode_pairs(const uint8_t* Q4, const uint8_t* S16, int R, int H, uint8_t* Q6, uint8_t* S32) {
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < R; ++r) {
+    const uint8_t* q4 = Q4 + (long)r * (H / 2);
+    const uint8_t* s16 = S16 + (long)r * (H / 16);
+    uint8_t* q6 = Q6 + (long)r * (3 * H / 4);
+    for (int b = 0; b < H / 32; ++b) {
+      int s0 = s16[2 * b], s1 = s16[2 * b + 1];
+      int E = (s0 > s1 ? s0 : s1) - 2;
+      if (E < 0) E = 0;
+      S32[(long)r * (H / 32) + b] = (uint8_t)E;
+      for (int j = 0; j < 32; ++j) {
+        int k = 32 * b + j;
+        int si = s16[k / 16];
+        double v = ldexp(orc_e2m1_decode(get_code(q4, k, ORC_MXFP4)), si - E);
+        put_code6(q6, k, orc_e3m2_encode(v));
+      }
+    }
+  }
+}
+
+/* Activations: §3.2 with G = 16 (m protected channels per 16-group, L may be
+ * NULL for none), then the pair re-encoding.  Q6: S x 3H/4, S32: S x H/32,
+ * B: S x (H/16 * m) as orc_quant_act_multi. */
+void orc_quant_act_fp6p(const uint16_t* X, int S, int H, const int32_t* L, int m, uint8_t* Q6, uint8_t* S32,
+                        uint16_t* B) {
+  uint8_t* q4 = (uint8_t*)calloc((size_t)S * (H / 2), 1);
+  uint8_t* s16 = (uint8_t*)calloc((size_t)S * (H / 16), 1);
+  if (L) orc_quant_act_multi(X, S, H, 16, L, m, ORC_MXFP4, q4, s16, B);
+  else orc_quant_act(X, S, H, 16, NULL, ORC_MXFP4, q4, s16, NULL);
+  reencode_pairs(q4, s16, S, H, Q6, S32);
+  free(q4);
+  free(s16);
+}
+
+/* Weights: unmodified W quantized as MXFP4 at G = 16 (W_L as the multi call),
+ * then re-encoded. */
+void orc_pack_weights_fp6p(const uint16_t* W, int N, int H, const int32_t* L, int m, uint8_t* Q6, uint8_t* S32,
+                           uint16_t* WL) {
+  uint8_t* q4 = (uint8_t*)calloc((size_t)N * (H / 2), 1);
+  uint8_t* s16 = (uint8_t*)calloc((size_t)N * (H / 16), 1);
+  if (L) orc_pack_weights_multi(W, N, H, 16, L, m, ORC_MXFP4, q4, s16, WL);
+  else orc_pack_weights(W, N, H, 16, NULL, ORC_MXFP4, q4, s16, NULL);
+  reencode_pairs(q4, s16, N, H, Q6, S32);
+  free(q4);
+  free(s16);
 }
