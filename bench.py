@@ -76,12 +76,12 @@ class Layer:
         side = lambda R: torch.empty((osc.side_elems(R, H, G, m),), dtype=torch.int16, device=dev)
         self.X = X_dev if X_dev is not None else torch.from_numpy(w.X.view(np.int16)).to(dev)
         self.QX = u8(osc.code_bytes(S, H, afmt))
-        self.SX = u8(osc.scale_bytes(S, H, G))
+        self.SX = u8(osc.scale_bytes(S, H, G, afmt))
         self.B = side(S) if L is not None else None
         if packed is None:
             Wd = torch.from_numpy(w.W.view(np.int16)).to(dev)
             self.QW = u8(osc.code_bytes(N, H, wfmt))
-            self.SW = u8(osc.scale_bytes(N, H, G))
+            self.SW = u8(osc.scale_bytes(N, H, G, wfmt))
             self.WL = side(N) if L is not None else None
             osc.osc_pack_weights_multi(Wd, N, H, G, L, m, wfmt, self.QW, self.SW, self.WL)  # offline, untimed
             del Wd
@@ -144,7 +144,10 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
 
     def gemm(l):
         P = l.ptr
-        if l.afmt == osc.OSC_MXFP4:
+        if l.afmt == osc.OSC_FP6P:
+            osc.osc_gemm_fp6p(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.m, P["Y"],
+                              osc.OSC_Y_BF16, s)
+        elif l.afmt == osc.OSC_MXFP4:
             osc.osc_gemm_multi(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, l.m, P["Y"],
                                osc.OSC_Y_BF16, s)
         else:
@@ -199,7 +202,10 @@ def time_layer_graph(torch, osc, sets, reps, stream):
 
     def gemm(l, s):
         P = l.ptr
-        if l.afmt == osc.OSC_MXFP4:
+        if l.afmt == osc.OSC_FP6P:
+            osc.osc_gemm_fp6p(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.m, P["Y"],
+                              osc.OSC_Y_BF16, s)
+        elif l.afmt == osc.OSC_MXFP4:
             osc.osc_gemm_multi(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, l.m, P["Y"],
                                osc.OSC_Y_BF16, s)
         else:
@@ -251,8 +257,9 @@ def gemm_bytes(w, afmt, wfmt, comp):
     """Algorithmic HBM bytes of one GEMM launch: every operand read once, Y (bf16) written once."""
     S, H, N, G = w.S, w.H, w.N, w.G
     K = H // G
-    cb = lambda f: 0.5 if f == 0 else 1.0
-    b = S * H * cb(afmt) + S * K + N * H * cb(wfmt) + N * K + 2 * S * N
+    cb = lambda f: 0.5 if f == 0 else 1.0 if f == 1 else 0.75
+    sb = lambda f: H // 32 if f == 2 else K  # scale bytes per row
+    b = S * H * cb(afmt) + S * sb(afmt) + N * H * cb(wfmt) + N * sb(wfmt) + 2 * S * N
     if comp:
         b += 2 * S * K + 2 * N * K
     return b
@@ -261,7 +268,8 @@ def gemm_bytes(w, afmt, wfmt, comp):
 def quant_bytes(w, afmt, extract):
     S, H, G = w.S, w.H, w.G
     K = H // G
-    return 2 * S * H + S * H * (0.5 if afmt == 0 else 1.0) + S * K + (2 * S * K if extract else 0)
+    cb = 0.5 if afmt == 0 else 1.0 if afmt == 1 else 0.75
+    return 2 * S * H + S * H * cb + S * (H // 32 if afmt == 2 else K) + (2 * S * K if extract else 0)
 
 
 def table_on_gpu(torch, osc, w, G, dev):
@@ -299,7 +307,8 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1)
     flops = 2.0 * w.S * w.H * w.N
     comp = L is not None
     row = {"workload": name, "S": w.S, "H": w.H, "N": w.N, "G": w.G,
-           "path": ("osc_mxfp4" if afmt == 0 else ("w8a4_fp8" if wfmt == 0 else "w8a8_fp8")),
+           "path": ("osc_mxfp4" if afmt == 0 else "osc_e3m2_pairs" if afmt == 2 else
+                    ("w8a4_fp8" if wfmt == 0 else "w8a8_fp8")),
            "protected_groups": None if L is None else int((np.asarray(L).reshape(-1, m) >= 0).any(axis=1).sum()),
            "protected_channels": None if L is None else int((np.asarray(L) >= 0).sum()), "m": m,
            "buffer_sets": len(sets), "timing": "hip_graph" if graphed else "eager", "ms_per_step": wall * 1e3,
@@ -623,6 +632,12 @@ def main():
                 if S == 16:
                     r["gemm_frac_of_hbm"] = r["gemm_gbs"] / PEAK_HBM_GBS
                 rows.append(r)
+                if G == 16 and S > 16:
+                    # the same layer with the 16-group pairs carried as E3M2 (one scale per 32)
+                    r6 = run_row(torch, osc, n + "_e3m2_pairs", ws, Ls, osc.OSC_FP6P, osc.OSC_FP6P, dev, stream,
+                                 100, 200)
+                    r6["speedup_vs_mxfp4_g16"] = r["ms_per_step"] / r6["ms_per_step"]
+                    rows.append(r6)
 
     # ---- quality side-measure (sampled rows, exact fp64 reference on the host)
     qual = None

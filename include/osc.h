@@ -35,6 +35,20 @@
  *       B, WL   panels of 32 groups: the bf16 of row r, group k is element
  *               (k/32 * R + r)*32 + k%32; ceil(K/32)*32*R elements, those of groups
  *               >= K are never written and never used.
+ *     OSC_FP6P (G = 16 only; "fast G = 16"): a scaled matrix instruction takes one
+ *     E8M0 scale per 32 elements, so the two 16-groups 2b, 2b+1 of an MXFP4 G = 16
+ *     quantization (codes c at their own scale codes s0, s1, extraction as usual)
+ *     travel as one scale code E = max(s0, s1) - 2 (at least 0) and 32 E3M2 codes
+ *     (OCP MX FP6 E3M2: bias 3, subnormals m/16, largest 28) of the values
+ *     dq(c) * 2^(s_i - E), rounded to nearest (ties to even code) -- exact while
+ *     |s0 - s1| <= 5.  A block's 32 codes form a 24-byte fragment, code i at bits
+ *     [6i, 6i+6) (little-endian).  Tiled: stage p (channels [128p, 128p+128), four
+ *     blocks) of R rows is R*96 bytes at p*R*96: first R x 64 bytes, row r holding
+ *     bytes 0..15 of block b's fragment at [16b, 16b+16); then R x 32 bytes, row r
+ *     holding bytes 16..23 of block b's fragment at [8*(b ^ ((r >> 3) & 3)), +8)
+ *     (rows XOR-permuted so 32 consecutive rows read without bank conflicts).  Codes
+ *     3*H*R/4 bytes; scales as G = 32 (panels of 4 blocks, R*H/32 bytes); B and WL
+ *     as G = 16 (K = H/16 groups).
   *   - L: HOST array of K int32 entries in {-1} ∪ [0, G), read during the call and
  *     passed to the kernels by value (kernel arguments), so a call can be captured
  *     in a HIP graph; K <= OSC_MAX_GROUPS.
@@ -72,7 +86,8 @@ typedef enum {
 
 typedef enum {
   OSC_MXFP4 = 0, /* E2M1 elements + E8M0 group scale */
-  OSC_MXFP8 = 1  /* E4M3 elements + E8M0 group scale */
+  OSC_MXFP8 = 1, /* E4M3 elements + E8M0 group scale */
+  OSC_FP6P = 2   /* G = 16 pairs: E3M2 elements + one E8M0 scale per two 16-groups (below) */
 } osc_fmt;
 
 typedef enum {
@@ -87,7 +102,7 @@ typedef enum {
  * osc_pack_weights -- offline weight preparation (§3.2 weight side, §3.3).
  *   W   [N][H] bf16, device.  Quantized unmodified along H in groups of G.
  *   L   host int32[K] table slice, or NULL (no compensation path: WL must be NULL).
- *   wfmt  OSC_MXFP4 or OSC_MXFP8.
+ *   wfmt  OSC_MXFP4, OSC_MXFP8, or OSC_FP6P (G = 16).
  *   QW  element codes, tiled (R = N), device, written.
  *   SW  E8M0 scales, tiled (R = N), device, written.
  *   WL  bf16, tiled (R = N), device, written: WL(n, k) = W[n][k*G + L[k]], or +0
@@ -103,7 +118,7 @@ osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L
  *   X   [S][H] bf16, device, read only (zeroing is logical).
  *   L   host int32[K] table slice, or NULL: no extraction (direct MX quantization,
  *       and the FP8 fallback of §4); then B must be NULL.
- *   afmt  OSC_MXFP4 or OSC_MXFP8.
+ *   afmt  OSC_MXFP4, OSC_MXFP8, or OSC_FP6P (G = 16).
  *   QX  element codes, tiled (R = S), device, written.
  *   SX  E8M0 scales, tiled (R = S), device, written; computed on the zeroed group.
  *   B   bf16, tiled (R = S), device, written: B(s, k) = X[s][k*G + L[k]] bit for
@@ -129,6 +144,23 @@ osc_status osc_quant_act(const void* X, int S, int H, int G, const int32_t* L, o
 osc_status osc_gemm(const void* QX, const uint8_t* SX, const void* B, const void* QW,
                     const uint8_t* SW, const void* WL, int S, int N, int H, int G, void* Y,
                     osc_ytype yt, void* stream);
+
+/*
+ * osc_gemm_fp6p -- the dual-path product at G = 16 on E3M2 pairs (format OSC_FP6P
+ * above; §3.3 Table 2's G = 16 at the matrix cores' FP4/FP6 issue rate):
+ *   Y[s][n] = sum_b 2^(EX(s,b) + EW(n,b)) * sum_{j<32} e3m2(qX) * e3m2(qW)
+ *           + sum_c B(s,c) * WL(n,c)      (c over m*H/16 compensation columns)
+ * which equals osc_gemm_multi at G = 16 whenever every pair is exact.
+ *   QX, SX, B  from osc_quant_act_multi(afmt = OSC_FP6P, G = 16);
+ *   QW, SW, WL from osc_pack_weights_multi(wfmt = OSC_FP6P, G = 16), same L and m;
+ *   B == WL == NULL: no compensation path.
+ *   Y   [S][N], bf16 or fp32 per yt, device, written.
+ * Constraints: S >= 0, N >= 0, H % 256 == 0, 1 <= m <= OSC_MAX_CHANNELS,
+ * m*H/16 <= OSC_MAX_GROUPS and (m*H/16) % 8 == 0 with compensation, S, N < 2^24,
+ * S * H and N * H < 2^34.  Every S runs the prefill kernel.
+ */
+osc_status osc_gemm_fp6p(const void* QX, const uint8_t* SX, const void* B, const void* QW, const uint8_t* SW,
+                         const void* WL, int S, int N, int H, int m, void* Y, osc_ytype yt, void* stream);
 
 /*
  * osc_gemm_fp8 -- the W2 fallback of §4: Y = (QX8 ⊗ QW)·S with E4M3 activations

@@ -42,7 +42,7 @@ def code_cols(H: int, fmt: int) -> int:
 
 def _tiled_outputs(R: int, H: int, G: int, fmt: int, with_side: bool, m: int = 1):
     Q = poisoned((osc.code_bytes(R, H, fmt),), torch.uint8)
-    SC = poisoned((osc.scale_bytes(R, H, G),), torch.uint8)
+    SC = poisoned((osc.scale_bytes(R, H, G, fmt),), torch.uint8)
     side = poisoned((osc.side_elems(R, H, G, m),), torch.int16) if with_side else None
     return Q, SC, side
 
@@ -150,4 +150,25 @@ def linear_decode(X_dev: torch.Tensor, S: int, H: int, G: int, L, m: int, QW, SW
                   yt=osc.OSC_Y_F32) -> torch.Tensor:
     Y = poisoned((S, N), torch.float32 if yt == osc.OSC_Y_F32 else torch.bfloat16)
     osc.osc_linear_decode(X_dev, S, H, G, L, m, QW, SW, WL, N, Y, yt)
+    return Y
+
+
+def codes6_rm(t: torch.Tensor, R: int, H: int) -> np.ndarray:
+    """tiled E3M2 pairs -> uint8[R, 3H/4] rows (element k at bits [6k, 6k+6)): per 128-channel
+    stage, the R x 64 first region holds bytes 0..15 of block b's 24-byte fragment at [16b, 16b+16),
+    the R x 32 second region bytes 16..23 at [8 * (b ^ ((r >> 3) & 3)), +8)."""
+    P = H // 128
+    a = host_u8(t).reshape(P, R * 96)
+    first = a[:, :R * 64].reshape(P, R, 4, 16)
+    second = a[:, R * 64:].reshape(P, R, 4, 8)
+    r = np.arange(R)[:, None]
+    pos = np.arange(4)[None, :] ^ ((r >> 3) & 3)          # [R, 4]: where block b's piece sits
+    second = second[:, r, pos, :]                            # [P, R, 4, 8] in block order
+    frag = np.concatenate([first, second], axis=3)           # [P, R, 4, 24]
+    return np.ascontiguousarray(frag.transpose(1, 0, 2, 3).reshape(R, P * 96))
+
+
+def gemm_fp6p(QX, SX, B, QW, SW, WL, S, N, H, m=1, yt=osc.OSC_Y_F32):
+    Y = poisoned((S, N), torch.float32 if yt == osc.OSC_Y_F32 else torch.bfloat16)
+    osc.osc_gemm_fp6p(QX, SX, B, QW, SW, WL, S, N, H, m, Y, yt)
     return Y

@@ -182,3 +182,17 @@ def test_linear_decode_validation():
     bad, bp = L8([0, 1, 2, 3, 4, 5, 6, 40])
     assert d(l=bp) == 3
     assert d(S=0) == 0 and d(N=0) == 0
+
+
+def test_fp6p_validation():
+    keep, lp = L8([-1] * 16)  # H=256, G=16: K=16
+    q = lambda G=16, f=2, l=lp, B=A: status("osc_quant_act_multi", A, 16, 256, G, l, 1, f, A, A, B, None)
+    assert q(G=32, l=L8([-1] * 8)[1]) == 5    # E3M2 pairs exist for G = 16 only
+    p = lambda G=16, f=2: status("osc_pack_weights_multi", A, 64, 256, G, None, 1, f, A, A, None, None)
+    assert p(G=64) == 5
+    g = lambda S=16, N=64, H=256, m=1, B=A, WL=A, yt=0: status("osc_gemm_fp6p", A, A, B, A, A, WL, S, N, H, m, A, yt,
+                                                                None)
+    assert g(H=384) == 2 and g(m=0) == 2 and g(yt=4) == 5
+    assert g(B=None) == 1
+    assert g(S=0) == 0
+    assert g(H=256 * 64 + 256) == 2          # H/16 > OSC_MAX_GROUPS

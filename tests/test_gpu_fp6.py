@@ -1,0 +1,133 @@
+"""GPU parity of the E3M2-pair path for G = 16 (osc_quant_act_multi / osc_pack_weights_multi with
+OSC_FP6P, osc_gemm_fp6p) against the oracle's pair re-encoding (tests/test_oracle_fp6.py pins it
+to the G = 16 MXFP4 oracle).  Codes, scales and B bit-exact -- including pairs whose scale codes
+differ by up to 9, where the smaller group rounds -- and Y within 2e-3 * (|Y| + RMS(Y))."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import w4a4_outlier_split_amd as osc  # noqa: E402
+from gpu_util import (assert_y_close, codes6_rm, dev_bits16, gemm_fp6p, gemm_multi, host_y, pack_multi,  # noqa: E402
+                      quant_multi, scales_rm, side_rm)
+
+FP6P = osc.OSC_FP6P
+
+
+def crafted_rows(rng, S, H):
+    """Every 32-channel pair gets a larger group with amax 2^a and a smaller one 2^(a - gap),
+    gap 0..9, values spread over every E2M1 magnitude of both groups, random signs."""
+    x = np.zeros((S, H))
+    mags = np.array([0.0, 0.3, 0.5, 0.8, 1.0, 1.25, 1.5, 2.0, 2.6, 3.0, 3.6, 4.0, 5.0, 6.0, 0.1, 0.2])
+    for s in range(S):
+        for b in range(H // 32):
+            a = int(rng.integers(-8, 8))
+            gap = int(rng.integers(0, 10))
+            big, small = (0, 1) if rng.random() < 0.5 else (1, 0)
+            for g, e in ((big, a), (small, a - gap)):
+                v = rng.permutation(mags) * 2.0 ** (e - 2)
+                v[0] = 6.0 * 2.0 ** (e - 2) * 1.2  # the group's amax lands in [4, 8) * 2^(e - 2)
+                x[s, 32 * b + 16 * g:32 * b + 16 * g + 16] = v * rng.choice([-1.0, 1.0], 16)
+    return to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("m", [0, 1, 2])
+@pytest.mark.parametrize("data", ["random", "crafted"])
+def test_quant_fp6p_bit_exact(m, data):
+    S, H = 37, 1024
+    rng = np.random.default_rng(10 * m + (data == "crafted"))
+    X = synth.random_bf16((S, H), seed=m + 1, scale=2.0) if data == "random" else crafted_rows(rng, S, H)
+    L = None
+    if m:
+        L = np.full((H // 16, m), -1, np.int32)
+        for k in range(H // 16):
+            L[k] = rng.choice(16, size=m, replace=False)
+    QX, SX, B = quant_multi(dev_bits16(X), S, H, 16, L, max(m, 1), FP6P) if m else \
+        _quant_plain(dev_bits16(X), S, H)
+    torch.cuda.synchronize()
+    rq, rs, rb = oracle.quant_act_fp6p(X, L, max(m, 1))
+    np.testing.assert_array_equal(codes6_rm(QX, S, H), rq)
+    np.testing.assert_array_equal(scales_rm(SX, S, H, 32), rs)
+    if m:
+        np.testing.assert_array_equal(side_rm(B, S, H, 16, m), rb)
+
+
+def _quant_plain(Xd, S, H):
+    from gpu_util import _tiled_outputs
+    QX, SX, _ = _tiled_outputs(S, H, 16, FP6P, False)
+    osc.osc_quant_act(Xd, S, H, 16, None, FP6P, QX, SX, None)
+    return QX, SX, None
+
+
+def test_pack_weights_fp6p_bit_exact():
+    N, H = 100, 512
+    W = synth.random_bf16((N, H), seed=9, scale=0.05)
+    L = np.random.default_rng(9).integers(-1, 16, (H // 16, 1)).astype(np.int32)
+    QW, SW, WL = pack_multi(dev_bits16(W), N, H, 16, L, 1, FP6P)
+    torch.cuda.synchronize()
+    rq, rs, rwl = oracle.pack_weights_fp6p(W, L, 1)
+    np.testing.assert_array_equal(codes6_rm(QW, N, H), rq)
+    np.testing.assert_array_equal(scales_rm(SW, N, H, 32), rs)
+    np.testing.assert_array_equal(side_rm(WL, N, H, 16, 1), rwl)
+
+
+@pytest.mark.parametrize("S,N,H,m", [(40, 96, 512, 1), (8, 64, 256, 2), (300, 520, 768, 1), (77, 200, 1024, 0),
+                                     (600, 1536, 512, 3)])
+def test_gemm_fp6p(S, N, H, m):
+    rng = np.random.default_rng(S + N + H + m)
+    X = synth.random_bf16((S, H), seed=S, scale=2.0)
+    W = synth.random_bf16((N, H), seed=N, scale=0.05)
+    L = None
+    if m:
+        L = np.full((H // 16, m), -1, np.int32)
+        for k in range(H // 16):
+            L[k] = rng.choice(16, size=m, replace=False)
+    mm = max(m, 1)
+    if m:
+        QX, SX, B = quant_multi(dev_bits16(X), S, H, 16, L, mm, FP6P)
+        QW, SW, WL = pack_multi(dev_bits16(W), N, H, 16, L, mm, FP6P)
+    else:
+        QX, SX, B = _quant_plain(dev_bits16(X), S, H)
+        from gpu_util import _tiled_outputs
+        QW, SW, WL = _tiled_outputs(N, H, 16, FP6P, False)
+        osc.osc_pack_weights(dev_bits16(W), N, H, 16, None, FP6P, QW, SW, None)
+    Y = gemm_fp6p(QX, SX, B, QW, SW, WL, S, N, H, mm)
+    torch.cuda.synchronize()
+    rqx, rsx, rb = oracle.quant_act_fp6p(X, L, mm)
+    rqw, rsw, rwl = oracle.pack_weights_fp6p(W, L, mm)
+    ref = oracle.gemm_fp6p(rqx, rsx, rqw, rsw, rb, rwl)
+    assert_y_close(host_y(Y), ref, what=f"fp6p S={S} N={N} H={H} m={m}")
+    # the same layer at G = 16 in MXFP4 (every pair exact on these inputs): same Y within tolerance
+    if m:
+        QX4, SX4, B4 = quant_multi(dev_bits16(X), S, H, 16, L, mm)
+        QW4, SW4, WL4 = pack_multi(dev_bits16(W), N, H, 16, L, mm)
+        Y4 = gemm_multi(QX4, SX4, B4, QW4, SW4, WL4, S, N, H, 16, mm)
+        torch.cuda.synchronize()
+        assert_y_close(host_y(Y), host_y(Y4), what="fp6p against the MXFP4 G=16 path")
+
+
+def test_gemm_fp6p_sweep_workload():
+    """The G-sweep workload at G = 16 (S = 8192, H = 4096, N = 6144, its table): sampled rows and
+    columns against the oracle, in the configuration the benchmark times."""
+    w = synth.group_sweep(8192, 16)
+    L, _, _ = oracle.build_table(w.calib, 16)
+    L2 = L.reshape(-1, 1)
+    QX, SX, B = quant_multi(dev_bits16(w.X), w.S, w.H, 16, L2, 1, FP6P)
+    QW, SW, WL = pack_multi(dev_bits16(w.W), w.N, w.H, 16, L2, 1, FP6P)
+    Y = gemm_fp6p(QX, SX, B, QW, SW, WL, w.S, w.N, w.H, 1)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(2).choice(w.S, 16, replace=False))
+    cols = np.sort(np.random.default_rng(3).choice(w.N, 512, replace=False))
+    rqx, rsx, rb = oracle.quant_act_fp6p(w.X[rows], L, 1)
+    rqw, rsw, rwl = oracle.pack_weights_fp6p(w.W[cols], L, 1)
+    ref = oracle.gemm_fp6p(rqx, rsx, rqw, rsw, rb, rwl)
+    got = Y.index_select(0, torch.from_numpy(rows).to(Y.device)).index_select(1, torch.from_numpy(cols).to(Y.device))
+    assert_y_close(got.double().cpu().numpy(), ref, what="fp6p G-sweep S=8192")

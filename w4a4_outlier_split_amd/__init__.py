@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "_build", "libosc.so")
 
 OSC_MXFP4 = 0
 OSC_MXFP8 = 1
+OSC_FP6P = 2  # G = 16 pairs: E3M2 codes, one E8M0 scale per 32 channels
 OSC_Y_BF16 = 0
 OSC_Y_F32 = 1
 OSC_MAX_GROUPS = 1024
@@ -36,7 +37,8 @@ STATUS = {0: "OSC_OK", 1: "OSC_E_NULL", 2: "OSC_E_SHAPE", 3: "OSC_E_TABLE", 4: "
 
 EXPORTS = ("osc_pack_weights", "osc_quant_act", "osc_gemm", "osc_gemm_fp8", "osc_build_table",
            "osc_pack_weights_multi", "osc_quant_act_multi", "osc_gemm_multi", "osc_build_table_multi",
-           "osc_swiglu_quant", "osc_swiglu", "osc_linear_decode", "osc_status_str", "osc_last_device_error")
+           "osc_swiglu_quant", "osc_swiglu", "osc_linear_decode", "osc_gemm_fp6p", "osc_status_str",
+           "osc_last_device_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libosc.so is not built ({LIB_PATH}); run python w4a4_outlier_split_amd/build.py")
@@ -57,6 +59,7 @@ _lib.osc_build_table_multi.argtypes = [_P, _I, _I, _I, _D, _D, _I, _P, _P, _P, _
 _lib.osc_swiglu_quant.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P]
 _lib.osc_swiglu.argtypes = [_P, _I, _I, _P, _P]
 _lib.osc_linear_decode.argtypes = [_P, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I, _P]
+_lib.osc_gemm_fp6p.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
 for _f in EXPORTS[:-2]:
     getattr(_lib, _f).restype = _I
 _lib.osc_status_str.argtypes = [_I]
@@ -67,12 +70,13 @@ _lib.osc_last_device_error.restype = ctypes.c_char_p
 
 def code_bytes(rows: int, H: int, fmt: int) -> int:
     """Bytes of a tiled code buffer (QX / QW) for ``rows`` rows of H channels."""
-    return rows * (H // 2 if fmt == OSC_MXFP4 else H)
+    return rows * (H // 2 if fmt == OSC_MXFP4 else H if fmt == OSC_MXFP8 else 3 * H // 4)
 
 
-def scale_bytes(rows: int, H: int, G: int) -> int:
-    """Bytes of a tiled E8M0 scale buffer (SX / SW): one per row and group."""
-    return rows * (H // G)
+def scale_bytes(rows: int, H: int, G: int, fmt: int = OSC_MXFP4) -> int:
+    """Bytes of a tiled E8M0 scale buffer (SX / SW): one per row and group (per pair of 16-groups
+    for OSC_FP6P)."""
+    return rows * (H // 32 if fmt == OSC_FP6P else H // G)
 
 
 def side_elems(rows: int, H: int, G: int, m: int = 1) -> int:
@@ -169,6 +173,12 @@ def osc_swiglu_quant(GU, S: int, F: int, G: int, L, m: int, afmt: int, QX, SX, B
     keep, lp = _table(L)
     _check(_lib.osc_swiglu_quant(_ptr(GU), S, F, G, lp, m, afmt, _ptr(QX), _ptr(SX), _ptr(B), _stream(stream)),
            "osc_swiglu_quant")
+
+
+def osc_gemm_fp6p(QX, SX, B, QW, SW, WL, S: int, N: int, H: int, m: int, Y, yt: int, stream=None) -> None:
+    """G = 16 on E3M2 pairs (operands from the quant / pack calls with fmt OSC_FP6P, G = 16)."""
+    _check(_lib.osc_gemm_fp6p(_ptr(QX), _ptr(SX), _ptr(B), _ptr(QW), _ptr(SW), _ptr(WL), S, N, H, m, _ptr(Y), yt,
+                              _stream(stream)), "osc_gemm_fp6p")
 
 
 def osc_linear_decode(X, S: int, H: int, G: int, L, m: int, QW, SW, WL, N: int, Y, yt: int, stream=None) -> None:

@@ -44,6 +44,9 @@ osc_status pack_table(const int32_t* L, int K, int m, int G, osc::TableArg* t) {
   return OSC_OK;
 }
 
+// element formats of the quantization calls: MXFP4, MXFP8, and the E3M2 pairs of G = 16
+bool valid_fmt(osc_fmt f, int G) { return f == OSC_MXFP4 || f == OSC_MXFP8 || (f == OSC_FP6P && G == 16); }
+
 bool valid_m(int m) { return m >= 1 && m <= osc::kMaxChannels; }
 
 // the HIP error behind the calling thread's most recent OSC_E_DEVICE
@@ -78,7 +81,7 @@ const char* osc_last_device_error(void) {
 
 osc_status osc_quant_act_multi(const void* X, int S, int H, int G, const int32_t* L, int m, osc_fmt afmt, void* QX,
                                uint8_t* SX, void* B, void* stream) {
-  if (afmt != OSC_MXFP4 && afmt != OSC_MXFP8) return OSC_E_FORMAT;
+  if (!valid_fmt(afmt, G)) return OSC_E_FORMAT;
   osc_status st = check_tiled(S, H, G);
   if (st != OSC_OK) return st;
   if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
@@ -111,7 +114,7 @@ osc_status osc_swiglu(const void* GU, int S, int F, void* Hout, void* stream) {
 
 osc_status osc_swiglu_quant(const void* GU, int S, int F, int G, const int32_t* L, int m, osc_fmt afmt, void* QX,
                             uint8_t* SX, void* B, void* stream) {
-  if (afmt != OSC_MXFP4 && afmt != OSC_MXFP8) return OSC_E_FORMAT;
+  if (!valid_fmt(afmt, G)) return OSC_E_FORMAT;
   osc_status st = check_tiled(S, F, G);
   if (st != OSC_OK) return st;
   if ((long long)S * (F / 4) > 0x7FFFFFFFLL) return OSC_E_SHAPE;  // the input rows are 2F wide
@@ -131,7 +134,7 @@ osc_status osc_swiglu_quant(const void* GU, int S, int F, int G, const int32_t* 
 
 osc_status osc_pack_weights_multi(const void* W, int N, int H, int G, const int32_t* L, int m, osc_fmt wfmt, void* QW,
                                   uint8_t* SW, void* WL, void* stream) {
-  if (wfmt != OSC_MXFP4 && wfmt != OSC_MXFP8) return OSC_E_FORMAT;
+  if (!valid_fmt(wfmt, G)) return OSC_E_FORMAT;
   osc_status st = check_tiled(N, H, G);
   if (st != OSC_OK) return st;
   if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
@@ -204,6 +207,23 @@ osc_status osc_linear_decode(const void* X, int S, int H, int G, const int32_t* 
   }
   osc::FusedArgs a{X, &tab, m, QW, SW, WL, Y, S, N, H, G, kc, yt};
   return from_hip(osc::launch_linear_dec(a, static_cast<hipStream_t>(stream)));
+}
+
+osc_status osc_gemm_fp6p(const void* QX, const uint8_t* SX, const void* B, const void* QW, const uint8_t* SW,
+                         const void* WL, int S, int N, int H, int m, void* Y, osc_ytype yt, void* stream) {
+  osc_status st = check_gemm(S, N, H, 16, yt);
+  if (st != OSC_OK) return st;
+  if (!valid_m(m) || (H / 16) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
+  if ((B == nullptr) != (WL == nullptr)) return OSC_E_NULL;
+  if (B && ((H / 16) * m) % 8 != 0) return OSC_E_SHAPE;
+  if (S == 0 || N == 0) return OSC_OK;
+  if (!QX || !SX || !QW || !SW || !Y) return OSC_E_NULL;
+  if (!aligned16(QX) || !aligned16(SX) || !aligned16(QW) || !aligned16(SW) || !aligned16(Y)) return OSC_E_ALIGN;
+  if (B && (!aligned16(B) || !aligned16(WL))) return OSC_E_ALIGN;
+  // the pairs' scale blocks are 32 wide: the kernels see G = 32 for the scales, the compensation
+  // keeps the G = 16 column count
+  osc::GemmArgs a{QX, SX, B, QW, SW, WL, Y, S, N, H, 32, B ? (H / 16) * m : 0, OSC_FP6P, OSC_FP6P, yt};
+  return from_hip(osc::launch_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
 osc_status osc_gemm_fp8(const void* QX8, const uint8_t* SX, const void* QW, const uint8_t* SW, osc_fmt wfmt, int S,

@@ -31,6 +31,74 @@ __device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us
 __device__ __forceinline__ uint32_t as_u32(us2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
 
+// ---- E3M2 pairs (G = 16 pairs carried by one scale per 32 elements)
+// E2M1 code c (at its 16-group's scale code) -> E3M2 code of the same value at the pair's scale
+// code, t = s_group - E_pair <= 2: the value 1.m * 2^p (p = -1 for 0.5) lands at exponent q = p + t;
+// q >= -2 is a normal E3M2 number, below that it is a multiple of 1/16 rounded to nearest, ties to
+// the even code (only when the pair's scale codes differ by more than 5).
+__device__ __forceinline__ uint32_t e2m1_to_e3m2(uint32_t c, int t) {
+  const uint32_t sign = (c & 8u) << 2;
+  const int mu = c & 7;
+  if (mu == 0) return sign;
+  const int p = mu == 1 ? -1 : (mu >> 1) - 1;
+  const int m = mu == 1 ? 0 : (mu & 1);
+  const int q = p + t;
+  if (q >= -2) return sign | (uint32_t)(((q + 3) << 2) | (m << 1));
+  const int units = q == -3 ? 2 + m : q == -4 ? (m ? 2 : 1) : q == -5 ? m : 0;  // of 1/16
+  return sign | (uint32_t)units;
+}
+
+// The lane's 8 E2M1 codes (one dword, channel 2i in the low nibble of byte i) -> the pair's E3M2
+// codes and its stores.  The four lanes of a quad hold one 32-element block (lanes 0-1: 16-group
+// 2b, lanes 2-3: 2b+1); lane q's 8 codes are bits [48q, 48q+48) of the block's 24-byte fragment.
+__device__ __forceinline__ void pair_store(uint32_t codes4, int sx, int r, int col0, int rows,
+                                           uint8_t* __restrict__ Q, uint8_t* __restrict__ SC) {
+  const int sx_other = __builtin_amdgcn_update_dpp(0, sx, 0x4E, 0xF, 0xF, false);  // the other 16-group
+  const int hi = sx > sx_other ? sx : sx_other;
+  const int E = hi > 2 ? hi - 2 : 0;
+  const int t = sx - E;
+  uint32_t lo = 0, hi16 = 0;  // 48 bits: lo = bits 0..31, hi16 = bits 32..47
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c6 = e2m1_to_e3m2((codes4 >> (4 * i)) & 15u, t);
+    const int bit = 6 * i;
+    if (bit + 6 <= 32) {
+      lo |= c6 << bit;
+    } else if (bit >= 32) {
+      hi16 |= c6 << (bit - 32);
+    } else {
+      lo |= c6 << bit;
+      hi16 |= c6 >> (32 - bit);
+    }
+  }
+  // every lane of the quad learns the four 48-bit pieces
+  const uint32_t lo0 = __builtin_amdgcn_update_dpp(0, lo, 0x00, 0xF, 0xF, false);
+  const uint32_t lo1 = __builtin_amdgcn_update_dpp(0, lo, 0x55, 0xF, 0xF, false);
+  const uint32_t lo2 = __builtin_amdgcn_update_dpp(0, lo, 0xAA, 0xF, 0xF, false);
+  const uint32_t lo3 = __builtin_amdgcn_update_dpp(0, lo, 0xFF, 0xF, 0xF, false);
+  const uint32_t h0 = __builtin_amdgcn_update_dpp(0, hi16, 0x00, 0xF, 0xF, false);
+  const uint32_t h1 = __builtin_amdgcn_update_dpp(0, hi16, 0x55, 0xF, 0xF, false);
+  const uint32_t h2 = __builtin_amdgcn_update_dpp(0, hi16, 0xAA, 0xF, 0xF, false);
+  const uint32_t h3 = __builtin_amdgcn_update_dpp(0, hi16, 0xFF, 0xF, 0xF, false);
+  const int q = (col0 >> 3) & 3;     // lane in the quad
+  const int b = (col0 & 127) >> 5;   // block in the stage
+  const long stage = (long)(col0 >> 7) * rows * 96;
+  // fragment dwords 0..3 (one per lane) -> the first R x 64 bytes of the stage
+  const uint32_t d = q == 0 ? lo0 : q == 1 ? (h0 | (lo1 << 16)) : q == 2 ? ((lo1 >> 16) | (h1 << 16)) : lo2;
+  __builtin_nontemporal_store(d, reinterpret_cast<uint32_t*>(Q + stage + (long)r * 64 + b * 16 + q * 4));
+  // dwords 4, 5 (lanes 0, 1) -> the R x 32 bytes after them, block position XOR-permuted by row
+  if (q < 2) {
+    const uint32_t e = q == 0 ? (h2 | (lo3 << 16)) : ((lo3 >> 16) | (h3 << 16));
+    __builtin_nontemporal_store(
+        e, reinterpret_cast<uint32_t*>(Q + stage + (long)rows * 64 + (long)r * 32 + 8 * (b ^ ((r >> 3) & 3)) + q * 4));
+  }
+  // one scale byte per block, at the G = 32 scale layout
+  if (q == 0) {
+    const int k32 = col0 >> 5;
+    SC[((long)(k32 >> 2) * rows + r) * 4 + (k32 & 3)] = (uint8_t)E;
+  }
+}
+
 // One 16-byte chunk c (8 bf16 of one row): extraction, group scale, encoding, tiled stores.
 template <int G, int FMT, int MODE, int M>
 __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, const TableArg& tab,
@@ -84,11 +152,19 @@ __device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, con
   if constexpr (LPG >= 4) amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0x4E, 0xF, 0xF, false));
   if constexpr (LPG >= 8) amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0x141, 0xF, 0xF, false));
   const int E = amax >> 7;
-  const int sx = FMT == OSC_MXFP4 ? (E > 2 ? E - 2 : 0) : (E > 8 ? E - 8 : 0);
-  if (q == 0) SC[scale_at] = (uint8_t)sx;
+  const int sx = FMT != OSC_MXFP8 ? (E > 2 ? E - 2 : 0) : (E > 8 ? E - 8 : 0);
+  if (FMT != OSC_FP6P && q == 0) SC[scale_at] = (uint8_t)sx;
   const float scale = __builtin_bit_cast(float, (uint32_t)sx << 23);  // only the exponent field is used
 
-  if (FMT == OSC_MXFP4) {
+  if constexpr (FMT == OSC_FP6P) {
+    static_assert(G == 16, "E3M2 pairs carry two 16-groups");
+    uint32_t out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w0), scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w1), scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w2), scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w3), scale, 3);
+    pair_store(out, sx, r, col0, rows, Q, SC);
+  } else if (FMT == OSC_MXFP4) {
     uint32_t out = 0;
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w0), scale, 0);
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w1), scale, 1);
@@ -254,6 +330,13 @@ hipError_t dispatch_mode(const void* X, int rows, int H, int m, const TableArg* 
 template <int G>
 hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* tab, int mode, osc_fmt fmt, bool glu,
                         void* Q, uint8_t* SC, void* side, hipStream_t st) {
+  if (fmt == OSC_FP6P) {
+    if constexpr (G == 16) {
+      if (glu) return dispatch_glu<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
+      return dispatch_mode<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
+    }
+    return hipErrorInvalidValue;  // E3M2 pairs exist for G = 16 only
+  }
   if (glu) {
     if (fmt == OSC_MXFP4) return dispatch_glu<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
     return dispatch_glu<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
