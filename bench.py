@@ -628,14 +628,14 @@ def main():
                     continue
                 ws = synth.group_sweep(S, G)
                 Ls = table_on_gpu(torch, osc, ws, G, dev)
-                r = run_row(torch, osc, n, ws, Ls, 0, 0, dev, stream, 100 if S > 16 else 200, 200)
+                r = run_row(torch, osc, n, ws, Ls, 0, 0, dev, stream, 100 if S > 16 else 200, 600 if S > 16 else 200)
                 if S == 16:
                     r["gemm_frac_of_hbm"] = r["gemm_gbs"] / PEAK_HBM_GBS
                 rows.append(r)
                 if G == 16 and S > 16:
                     # the same layer with the 16-group pairs carried as E3M2 (one scale per 32)
                     r6 = run_row(torch, osc, n + "_e3m2_pairs", ws, Ls, osc.OSC_FP6P, osc.OSC_FP6P, dev, stream,
-                                 100, 200)
+                                 100, 600)
                     r6["speedup_vs_mxfp4_g16"] = r["ms_per_step"] / r6["ms_per_step"]
                     rows.append(r6)
 

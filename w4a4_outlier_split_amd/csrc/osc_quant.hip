@@ -58,17 +58,37 @@ __device__ __forceinline__ void pair_store(uint32_t codes4, int sx, int r, int c
   const int E = hi > 2 ? hi - 2 : 0;
   const int t = sx - E;
   uint32_t lo = 0, hi16 = 0;  // 48 bits: lo = bits 0..31, hi16 = bits 32..47
+  if (t >= -1) {
+    // groups within 3 scale codes of each other: every nonzero magnitude lands on a normal E3M2
+    // number, code = base(mu) + 4t with base = 8 for 0.5 and 2 mu + 8 above -- four codes per
+    // dword, one byte each (a byte permute looks up the base)
+    auto bytes = [](uint32_t n) {  // 4 nibbles -> 4 bytes
+      return (n & 0xFu) | ((n & 0xF0u) << 4) | ((n & 0xF00u) << 8) | ((n & 0xF000u) << 12);
+    };
+    auto conv = [&](uint32_t e) {
+      const uint32_t mu = e & 0x07070707u;
+      const uint32_t base = __builtin_amdgcn_perm(0x16141210u, 0x0E0C0800u, mu);
+      const uint32_t nz = __builtin_amdgcn_perm(0x01010101u, 0x01010100u, mu);
+      const uint32_t c = t >= 0 ? base + nz * (uint32_t)(4 * t) : base - nz * 4u;
+      const uint32_t x = c | ((e & 0x08080808u) << 2);  // sign bit 3 -> 5
+      return (x & 0x3Fu) | ((x >> 2) & 0xFC0u) | ((x >> 4) & 0x3F000u) | ((x >> 6) & 0xFC0000u);  // 4 x 6 bits
+    };
+    const uint32_t a = conv(bytes(codes4 & 0xFFFFu)), b = conv(bytes(codes4 >> 16));
+    lo = a | (b << 24);
+    hi16 = b >> 8;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c6 = e2m1_to_e3m2((codes4 >> (4 * i)) & 15u, t);
-    const int bit = 6 * i;
-    if (bit + 6 <= 32) {
-      lo |= c6 << bit;
-    } else if (bit >= 32) {
-      hi16 |= c6 << (bit - 32);
-    } else {
-      lo |= c6 << bit;
-      hi16 |= c6 >> (32 - bit);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c6 = e2m1_to_e3m2((codes4 >> (4 * i)) & 15u, t);
+      const int bit = 6 * i;
+      if (bit + 6 <= 32) {
+        lo |= c6 << bit;
+      } else if (bit >= 32) {
+        hi16 |= c6 << (bit - 32);
+      } else {
+        lo |= c6 << bit;
+        hi16 |= c6 >> (32 - bit);
+      }
     }
   }
   // every lane of the quad learns the four 48-bit pieces
