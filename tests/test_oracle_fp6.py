@@ -8,6 +8,7 @@ magnitudes, monotone, sign bit 5) and round trips; ties to even; reduction to th
 G = 16 MXFP4 oracle -- every decoded E3M2 value times its pair scale equals the MXFP4 value times its
 group scale, and the whole GEMM equals the G = 16 OSC GEMM in fp64, whenever the two groups' scale
 codes differ by at most 5; a hand-built pair with a gap of 7 whose smaller group rounds."""
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -25,11 +26,14 @@ def test_e3m2_grid():
     assert all(a < b for a, b in zip(mags, mags[1:]))
     for c in range(32):
         assert oracle.e3m2_decode(c | 32) == -mags[c]
-        # every normal value has a 2-bit mantissa: 4 * v / 2^floor(log2 v) is an integer in [4, 8)
+        v = Fraction(mags[c])
         if c >= 4:
-            f = Fraction(mags[c]) / Fraction(2) ** (Fraction(mags[c]).numerator.bit_length()
-                                                     - Fraction(mags[c]).denominator.bit_length())
-            assert f.denominator in (1, 2, 4)
+            # a normal value: 2^e * (1 + m/4) with e in [-2, 4] and a 2-bit mantissa m
+            e = math.floor(math.log2(mags[c]))
+            f = v / Fraction(2) ** e
+            assert -2 <= e <= 4 and 1 <= f < 2 and (4 * f).denominator == 1
+        else:
+            assert v == Fraction(c, 16)  # subnormals: multiples of 1/16
 
 
 def test_e3m2_encode_round_trip_ties_and_saturation():
