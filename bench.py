@@ -131,28 +131,34 @@ class TimingEvents:
             self.hip.hipEventDestroy(h)
 
 
+def step_quant(osc, l, s):
+    """The step's first launch: osc_quant_act_multi on layer l's buffers, on stream handle s."""
+    P = l.ptr
+    osc.osc_quant_act_multi(P["X"], l.S, l.H, l.G, l.L, l.m, l.afmt, P["QX"], P["SX"], P["B"], s)
+
+
+def step_gemm(osc, l, s):
+    """The step's second launch: the GEMM entry point for layer l's operand formats."""
+    P = l.ptr
+    if l.afmt == osc.OSC_FP6P:
+        osc.osc_gemm_fp6p(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.m, P["Y"],
+                          osc.OSC_Y_BF16, s)
+    elif l.afmt == osc.OSC_MXFP4:
+        osc.osc_gemm_multi(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, l.m, P["Y"],
+                           osc.OSC_Y_BF16, s)
+    else:
+        osc.osc_gemm_fp8(P["QX"], P["SX"], P["QW"], P["SW"], l.wfmt, l.S, l.N, l.H, l.G, P["Y"],
+                         osc.OSC_Y_BF16, s)
+
+
 def time_layer(torch, osc, sets, steps, warmup, stream):
     """Run quant + GEMM over rotating buffer sets.  The steps run back to back under one event
     pair (the step time); a second pass with an event between the two kernels of every step gives
     the quant / GEMM split.  Returns seconds per step (events), seconds per step (host clock around
     the first pass) and the average event-timed durations of the quant and GEMM kernels."""
     s = stream.cuda_stream
-
-    def quant(l):
-        P = l.ptr
-        osc.osc_quant_act_multi(P["X"], l.S, l.H, l.G, l.L, l.m, l.afmt, P["QX"], P["SX"], P["B"], s)
-
-    def gemm(l):
-        P = l.ptr
-        if l.afmt == osc.OSC_FP6P:
-            osc.osc_gemm_fp6p(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.m, P["Y"],
-                              osc.OSC_Y_BF16, s)
-        elif l.afmt == osc.OSC_MXFP4:
-            osc.osc_gemm_multi(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, l.m, P["Y"],
-                               osc.OSC_Y_BF16, s)
-        else:
-            osc.osc_gemm_fp8(P["QX"], P["SX"], P["QW"], P["SW"], l.wfmt, l.S, l.N, l.H, l.G, P["Y"],
-                             osc.OSC_Y_BF16, s)
+    quant = lambda l: step_quant(osc, l, s)
+    gemm = lambda l: step_gemm(osc, l, s)
 
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -196,21 +202,8 @@ def time_layer_graph(torch, osc, sets, reps, stream):
     graph, and reps quantizations / reps GEMMs into two more (and, for MXFP4 activations, reps
     one-launch layers, osc_linear_decode, into a fourth), and time one replay of each.
     Returns seconds per step, per quantization, per GEMM (and per fused layer, or None)."""
-    def quant(l, s):
-        P = l.ptr
-        osc.osc_quant_act_multi(P["X"], l.S, l.H, l.G, l.L, l.m, l.afmt, P["QX"], P["SX"], P["B"], s)
-
-    def gemm(l, s):
-        P = l.ptr
-        if l.afmt == osc.OSC_FP6P:
-            osc.osc_gemm_fp6p(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.m, P["Y"],
-                              osc.OSC_Y_BF16, s)
-        elif l.afmt == osc.OSC_MXFP4:
-            osc.osc_gemm_multi(P["QX"], P["SX"], P["B"], P["QW"], P["SW"], P["WL"], l.S, l.N, l.H, l.G, l.m, P["Y"],
-                               osc.OSC_Y_BF16, s)
-        else:
-            osc.osc_gemm_fp8(P["QX"], P["SX"], P["QW"], P["SW"], l.wfmt, l.S, l.N, l.H, l.G, P["Y"],
-                             osc.OSC_Y_BF16, s)
+    quant = lambda l, s: step_quant(osc, l, s)
+    gemm = lambda l, s: step_gemm(osc, l, s)
 
     def fused(l, s):
         P = l.ptr
@@ -240,6 +233,72 @@ def time_layer_graph(torch, osc, sets, reps, stream):
     if len(out) == 3:
         out.append(None)
     return tuple(out)
+
+
+def sclk_file():
+    """The amdgpu clock-level file of the GPU: pp_dpm_sclk lists the gfx clock levels and marks the
+    current one (sampled by the firmware) with '*'.  None unless exactly one card exposes it."""
+    import glob
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return files[0] if len(files) == 1 else None
+
+
+def read_sclk_mhz(path):
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.endswith("*"):
+                return float(line.split(":", 1)[1].lower().split("mhz")[0])
+    return None
+
+
+def clock_pass(torch, osc, sets, stream, t_step, seconds=0.3, period=0.005, skip=0.05):
+    """Gfx clock while the step runs: a pass of its own after the timed ones (so sampling cannot
+    disturb them).  Enqueues about `seconds` of steps while a host thread reads the clock-level
+    file every `period` s; samples from the first `skip` s and after the GPU has drained are
+    dropped.  Returns {median, min, max, samples, source} in MHz, or None where unreadable."""
+    import threading
+    path = sclk_file()
+    if path is None:
+        return None
+    try:
+        read_sclk_mhz(path)
+    except OSError:
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t = time.perf_counter()
+            try:
+                v = read_sclk_mhz(path)
+            except (OSError, ValueError, IndexError):
+                v = None
+            samples.append((t, v))
+            time.sleep(period)
+
+    s = stream.cuda_stream
+    n = max(1, int(seconds / t_step))
+    th = threading.Thread(target=sampler, daemon=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        th.start()
+        for i in range(n):
+            l = sets[i % len(sets)]
+            step_quant(osc, l, s)
+            step_gemm(osc, l, s)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    stop.set()
+    th.join()
+    mhz = sorted(v for t, v in samples if v is not None and t0 + skip <= t <= t1)
+    if not mhz:
+        return None
+    return {"median": mhz[len(mhz) // 2], "min": mhz[0], "max": mhz[-1], "samples": len(mhz),
+            "source": f"{path} ('*' level), every {period * 1e3:.0f} ms over {n} back-to-back steps "
+                      f"({t1 - t0:.2f} s; first {skip * 1e3:.0f} ms dropped), a pass after the timed ones"}
 
 
 def make_sets(torch, osc, w, L, afmt, wfmt, dev, m=1):
@@ -294,7 +353,7 @@ def table_on_gpu_multi(torch, osc, w, G, m, dev):
     return L.cpu().numpy().reshape(K, m)
 
 
-def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1):
+def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1, clock=False):
     import numpy as np
     sets = make_sets(torch, osc, w, L, afmt, wfmt, dev, m)
     graphed = w.S <= 32  # decode shapes: kernels shorter than the host's enqueue time
@@ -304,6 +363,7 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1)
         host = wall
     else:
         wall, host, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
+    sclk = clock_pass(torch, osc, sets, stream, wall) if clock else None
     flops = 2.0 * w.S * w.H * w.N
     comp = L is not None
     row = {"workload": name, "S": w.S, "H": w.H, "N": w.N, "G": w.G,
@@ -324,6 +384,8 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1)
         fb = 2 * w.S * w.H + w.N * w.H / 2 + w.N * K + (2 * w.N * K * m if comp else 0) + 2 * w.S * w.N
         row["fused_gbs"] = fb / tf / 1e9  # X read, packed weights read, Y written
         row["fused_speedup"] = wall / tf
+    if clock:
+        row["sclk_mhz"] = sclk
     peak = PEAK_TFLOPS["mxfp4"] if afmt == 0 else PEAK_TFLOPS["fp8"]
     row["gemm_frac_of_peak"] = row["gemm_tflops"] / peak
     row["frac_of_mxfp4_peak"] = row["tflops"] / PEAK_TFLOPS["mxfp4"]
@@ -572,7 +634,7 @@ def main():
     head = None
     if args.only in (None, "qkv"):
         head = run_row(torch, osc, "qkv_proj_s2048_g32", w, L, osc.OSC_MXFP4, osc.OSC_MXFP4, dev, stream,
-                       args.steps, args.warmup)
+                       args.steps, args.warmup, clock=True)
 
     # ---- the W8A8 comparator of the pages' speedup table, same shape: MXFP8 activations and
     # weights, no extraction
@@ -675,6 +737,13 @@ def main():
                 "frac": achieved / PEAK_TFLOPS["mxfp4"], "traffic": traffic,
                 "kernel": "k_gemm (osc_gemm, MXFP4 scaled MFMA + fused bf16 compensation)",
                 "flops_per_launch": gemm_flops, "avg_launch_us": head["t_gemm_us"]}
+    sclk = head.get("sclk_mhz")
+    if sclk:
+        # the same launch against the MFMA rate at the clock the chip ran during the step (the
+        # published peak assumes 2.4 GHz); context beside frac, which stays on the published peak
+        at = PEAK_TFLOPS["mxfp4"] * sclk["median"] / 2400.0
+        roofline["peak_at_measured_sclk"] = at
+        roofline["frac_at_measured_sclk"] = achieved / at
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -692,6 +761,7 @@ def main():
                    "table": "built on the GPU (osc_build_table) from 1536 seeded calibration rows"},
         "frac_of_mxfp4_peak": head["tflops"] / PEAK_TFLOPS["mxfp4"],
         "t_quant_us": head["t_quant_us"], "t_gemm_us": head["t_gemm_us"],
+        "sclk_mhz": head.get("sclk_mhz"),
         "roofline": roofline,
         "quant_roofline": {"bound": "hbm", "achieved": head["quant_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": head["quant_gbs"] / PEAK_HBM_GBS},
