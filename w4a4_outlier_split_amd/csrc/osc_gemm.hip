@@ -55,10 +55,13 @@ constexpr int kFp6 = 3;  // E3M2 (the G = 16 pairs)
 __device__ __forceinline__ v8i widen(v4i lo) { return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1); }
 __device__ __forceinline__ v8i join(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
 
-// swizzled position of logical 16-byte chunk cc in LDS row r, for rows of RB bytes
+// swizzled position of logical 16-byte chunk cc in LDS row r, for rows of RB bytes.  64-byte rows:
+// the chunk index is XORed with bits 2-3 of the row (chosen by measurement: SQ_LDS_BANK_CONFLICT of
+// the QKV GEMM falls from ~4 to ~0.3 cycles per fragment read against XOR with bits 1 and 3, and
+// with bits 0-1 it is ~12).
 template <int RB>
 __device__ __forceinline__ int swz(int r, int cc) {
-  if constexpr (RB == 64) return cc ^ (((r >> 1) ^ (r >> 3)) & 3);
+  if constexpr (RB == 64) return cc ^ ((r >> 2) & 3);
   else return cc ^ ((r ^ (r >> 3)) & 7);
 }
 
