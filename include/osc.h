@@ -45,8 +45,9 @@
  *     [6i, 6i+6) (little-endian).  Tiled: stage p (channels [128p, 128p+128), four
  *     blocks) of R rows is R*96 bytes at p*R*96: first R x 64 bytes, row r holding
  *     bytes 0..15 of block b's fragment at [16b, 16b+16); then R x 32 bytes, row r
- *     holding bytes 16..23 of block b's fragment at [8*(b ^ ((r >> 3) & 3)), +8)
- *     (rows XOR-permuted so 32 consecutive rows read without bank conflicts).  Codes
+ *     holding bytes 16..23 of block b's fragment at [8*(b ^ (((r >> 1) ^ (r >> 3)) & 3)),
+ *     +8) (pieces XOR-permuted by row so that the GEMM's 8-byte reads of 32
+ *     consecutive rows spread over the LDS banks).  Codes
  *     3*H*R/4 bytes; scales as G = 32 (panels of 4 blocks, R*H/32 bytes); B and WL
  *     as G = 16 (K = H/16 groups).
   *   - L: HOST array of K int32 entries in {-1} ∪ [0, G), read during the call and

@@ -156,13 +156,13 @@ def linear_decode(X_dev: torch.Tensor, S: int, H: int, G: int, L, m: int, QW, SW
 def codes6_rm(t: torch.Tensor, R: int, H: int) -> np.ndarray:
     """tiled E3M2 pairs -> uint8[R, 3H/4] rows (element k at bits [6k, 6k+6)): per 128-channel
     stage, the R x 64 first region holds bytes 0..15 of block b's 24-byte fragment at [16b, 16b+16),
-    the R x 32 second region bytes 16..23 at [8 * (b ^ ((r >> 3) & 3)), +8)."""
+    the R x 32 second region bytes 16..23 at [8 * (b ^ (((r >> 1) ^ (r >> 3)) & 3)), +8)."""
     P = H // 128
     a = host_u8(t).reshape(P, R * 96)
     first = a[:, :R * 64].reshape(P, R, 4, 16)
     second = a[:, R * 64:].reshape(P, R, 4, 8)
     r = np.arange(R)[:, None]
-    pos = np.arange(4)[None, :] ^ ((r >> 3) & 3)          # [R, 4]: where block b's piece sits
+    pos = np.arange(4)[None, :] ^ (((r >> 1) ^ (r >> 3)) & 3)          # [R, 4]: where block b's piece sits
     second = second[:, r, pos, :]                            # [P, R, 4, 8] in block order
     frag = np.concatenate([first, second], axis=3)           # [P, R, 4, 24]
     return np.ascontiguousarray(frag.transpose(1, 0, 2, 3).reshape(R, P * 96))

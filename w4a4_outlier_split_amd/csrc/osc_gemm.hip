@@ -403,7 +403,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
         } else if constexpr (FA == kFp6) {
           // block 2m+h's 24-byte fragment: 16 bytes from the first region, 8 from the second
           f.alo[sm][i] = lds4(As + r * 64 + swz<64>(r, 2 * m + h) * 16);
-          const v2i d = lds2(QAs + r * 32 + 8 * ((2 * m + h) ^ ((r >> 3) & 3)));
+          const v2i d = lds2(QAs + r * 32 + 8 * ((2 * m + h) ^ (((r >> 1) ^ (r >> 3)) & 3)));
           f.ahi[sm][i] = v4i{d[0], d[1], 0, 0};
         } else {
           f.alo[sm][i] = lds4(As + r * 128 + swz<128>(r, 4 * m + h) * 16);
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
           }
         } else if constexpr (FB == kFp6) {
           f.blo[sm][j] = lds4(Bs + r * 64 + swz<64>(r, 2 * m + h) * 16);
-          const v2i d = lds2(QBs + r * 32 + 8 * ((2 * m + h) ^ ((r >> 3) & 3)));
+          const v2i d = lds2(QBs + r * 32 + 8 * ((2 * m + h) ^ (((r >> 1) ^ (r >> 3)) & 3)));
           f.bhi[sm][j] = v4i{d[0], d[1], 0, 0};
         } else {
           f.blo[sm][j] = lds4(Bs + r * 128 + swz<128>(r, 4 * m + h) * 16);

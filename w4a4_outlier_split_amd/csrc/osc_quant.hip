@@ -110,7 +110,7 @@ __device__ __forceinline__ void pair_store(uint32_t codes4, int sx, int r, int c
   if (q < 2) {
     const uint32_t e = q == 0 ? (h2 | (lo3 << 16)) : ((lo3 >> 16) | (h3 << 16));
     __builtin_nontemporal_store(
-        e, reinterpret_cast<uint32_t*>(Q + stage + (long)rows * 64 + (long)r * 32 + 8 * (b ^ ((r >> 3) & 3)) + q * 4));
+        e, reinterpret_cast<uint32_t*>(Q + stage + (long)rows * 64 + (long)r * 32 + 8 * (b ^ (((r >> 1) ^ (r >> 3)) & 3)) + q * 4));
   }
   // one scale byte per block, at the G = 32 scale layout
   if (q == 0) {
