@@ -377,15 +377,16 @@ __global__ __launch_bounds__(kWaves * 64) void k_linear_dec(const u4* __restrict
   // Prologue.  Thread t owns the 8-channel chunk column t (then t + 512, ...) of X.  Its loads of
   // the first kXRows rows and its group's table entries are issued first, then the wavefront's
   // weight loads; the loads complete in order, so the quantization of those rows waits for X only
-  // and runs while the weights stream in.
+  // and runs while the weights stream in.  The X loads are unconditional (rows past S reload row
+  // S-1, never used): a load under a row test is issued after the weight loads and then waits for
+  // them.  They go through the L2, which every workgroup on the XCD shares: each reads all of X.
   constexpr int kXRows = 16;
   const int cpr = H >> 3;
   u4 xv[kXRows];
   int ent0[M];
   if (tid < cpr) {
 #pragma unroll
-    for (int r = 0; r < kXRows; ++r)
-      if (r < S) xv[r] = __builtin_nontemporal_load(X + (long)r * cpr + tid);
+    for (int r = 0; r < kXRows; ++r) xv[r] = X[(long)min(r, S - 1) * cpr + tid];
 #pragma unroll
     for (int e = 0; e < M; ++e) ent0[e] = COMP ? tab.v[(tid * 8 / G) * M + e] : -1;
   }
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_linear_dec(const u4* __restrict
 #pragma unroll
     for (int e = 0; e < M; ++e) ent[e] = COMP ? tab.v[(j * 8 / G) * M + e] : -1;
     for (int r = (j == tid ? kXRows : 0); r < S; ++r)
-      quant_chunk_lds<G, M, COMP>(__builtin_nontemporal_load(X + (long)r * cpr + j), r, j * 8, ent, codes, scl, side);
+      quant_chunk_lds<G, M, COMP>(X[(long)r * cpr + j], r, j * 8, ent, codes, scl, side);
   }
   zero_rows<G, COMP>(S, H, KC, codes, scl, side);
   __syncthreads();
