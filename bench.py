@@ -353,7 +353,7 @@ def table_on_gpu_multi(torch, osc, w, G, m, dev):
     return L.cpu().numpy().reshape(K, m)
 
 
-def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1, clock=False):
+def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1, clock=True):
     import numpy as np
     sets = make_sets(torch, osc, w, L, afmt, wfmt, dev, m)
     graphed = w.S <= 32  # decode shapes: kernels shorter than the host's enqueue time
@@ -363,6 +363,7 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1,
         host = wall
     else:
         wall, host, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
+    clock = clock and not graphed  # graph-timed rows are launch-bound: no clock of interest
     sclk = clock_pass(torch, osc, sets, stream, wall) if clock else None
     flops = 2.0 * w.S * w.H * w.N
     comp = L is not None
