@@ -155,7 +155,8 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
     """Run quant + GEMM over rotating buffer sets.  The steps run back to back under one event
     pair (the step time); a second pass with an event between the two kernels of every step gives
     the quant / GEMM split.  Returns seconds per step (events), seconds per step (host clock around
-    the first pass) and the average event-timed durations of the quant and GEMM kernels."""
+    the first pass), the average event-timed durations of the quant and GEMM kernels, and their
+    medians and minima (microseconds) over the steps of the second pass."""
     s = stream.cuda_stream
     quant = lambda l: step_quant(osc, l, s)
     gemm = lambda l: step_gemm(osc, l, s)
@@ -177,6 +178,7 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
             quant(l)
             gemm(l)
         ev.record(2 * steps + 2, s)
+        t_enq = time.perf_counter()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         # pass 2: the split between the two kernels
@@ -190,10 +192,13 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
         torch.cuda.synchronize()
         gc.enable()
     t_step = ev.ms(2 * steps + 1, 2 * steps + 2) / steps * 1e-3
-    tq = sum(ev.ms(2 * i, 2 * i + 1) for i in range(steps)) / steps * 1e-3
-    tg = sum(ev.ms(2 * i + 1, 2 * i + 2) for i in range(steps)) / steps * 1e-3
+    q = sorted(ev.ms(2 * i, 2 * i + 1) * 1e-3 for i in range(steps))
+    g = sorted(ev.ms(2 * i + 1, 2 * i + 2) * 1e-3 for i in range(steps))
     ev.close()
-    return t_step, (t1 - t0) / steps, tq, tg
+    spread = {"t_quant_us_median": q[steps // 2] * 1e6, "t_quant_us_min": q[0] * 1e6,
+              "t_gemm_us_median": g[steps // 2] * 1e6, "t_gemm_us_min": g[0] * 1e6,
+              "host_enqueue_us_per_step": (t_enq - t0) / steps * 1e6}
+    return t_step, (t1 - t0) / steps, sum(q) / steps, sum(g) / steps, spread
 
 
 def time_layer_graph(torch, osc, sets, reps, stream):
@@ -358,11 +363,12 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1,
     sets = make_sets(torch, osc, w, L, afmt, wfmt, dev, m)
     graphed = w.S <= 32  # decode shapes: kernels shorter than the host's enqueue time
     tf = None
+    spread = None
     if graphed:
         wall, tq, tg, tf = time_layer_graph(torch, osc, sets, steps, stream)
         host = wall
     else:
-        wall, host, tq, tg = time_layer(torch, osc, sets, steps, warmup, stream)
+        wall, host, tq, tg, spread = time_layer(torch, osc, sets, steps, warmup, stream)
     clock = clock and not graphed  # graph-timed rows are launch-bound: no clock of interest
     sclk = clock_pass(torch, osc, sets, stream, wall) if clock else None
     flops = 2.0 * w.S * w.H * w.N
@@ -378,6 +384,8 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1,
            "gemm_tflops": flops / tg / 1e12,
            "quant_gbs": quant_bytes(w, afmt, comp) / tq / 1e9,
            "gemm_gbs": gemm_bytes(w, afmt, wfmt, comp) / tg / 1e9}
+    if spread:
+        row.update(spread)
     if tf is not None:
         # the same layer as one launch (quantization fused into the decode GEMM)
         row["fused_ms_per_step"] = tf * 1e3
@@ -754,7 +762,8 @@ def main():
     out = {
         "metric": "fused OSC W4A4 quant+GEMM TFLOP/s at Qwen3-8B shapes; % of MXFP4 MFMA peak",
         "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": ms, "host_ms_per_step": head["host_ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4", "data": "synthetic",
         "config": {"workload": "Qwen3-8B QKV projection, one OSC W4A4 linear layer: S=2048 tokens, H=4096, "
                                "N=6144, G=32", "S": w.S, "H": w.H, "N": w.N, "G": w.G,
@@ -762,6 +771,8 @@ def main():
                    "table": "built on the GPU (osc_build_table) from 1536 seeded calibration rows"},
         "frac_of_mxfp4_peak": head["tflops"] / PEAK_TFLOPS["mxfp4"],
         "t_quant_us": head["t_quant_us"], "t_gemm_us": head["t_gemm_us"],
+        "t_gemm_us_median": head.get("t_gemm_us_median"), "t_gemm_us_min": head.get("t_gemm_us_min"),
+        "host_enqueue_us_per_step": head.get("host_enqueue_us_per_step"),
         "sclk_mhz": head.get("sclk_mhz"),
         "roofline": roofline,
         "quant_roofline": {"bound": "hbm", "achieved": head["quant_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
