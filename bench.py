@@ -36,6 +36,17 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}  # MI355X dense, published
 PEAK_HBM_GBS = 8000.0
+
+
+def gemm_peak_tflops(afmt, wfmt):
+    """Published dense peak of the scaled MFMA a GEMM of these operand formats issues.
+
+    The instruction runs at the rate of its wider operand: E2M1 x E2M1 and the E3M2 pairs
+    (FP6 issues at the FP4 rate on gfx950) at the MXFP4 peak; anything with an E4M3 operand
+    at the FP8 peak.  Formats: 0 = MXFP4, 1 = MXFP8 (E4M3), 2 = E3M2 pairs."""
+    if afmt == 1 or wfmt == 1:
+        return PEAK_TFLOPS["fp8"]
+    return PEAK_TFLOPS["mxfp4"]
 MALL_BYTES = 256 << 20
 
 
@@ -395,8 +406,7 @@ def run_row(torch, osc, name, w, L, afmt, wfmt, dev, stream, steps, warmup, m=1,
         row["fused_speedup"] = wall / tf
     if clock:
         row["sclk_mhz"] = sclk
-    peak = PEAK_TFLOPS["mxfp4"] if afmt == 0 else PEAK_TFLOPS["fp8"]
-    row["gemm_frac_of_peak"] = row["gemm_tflops"] / peak
+    row["gemm_frac_of_peak"] = row["gemm_tflops"] / gemm_peak_tflops(afmt, wfmt)
     row["frac_of_mxfp4_peak"] = row["tflops"] / PEAK_TFLOPS["mxfp4"]
     del sets
     torch.cuda.empty_cache()

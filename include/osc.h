@@ -75,7 +75,15 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations travel as int.  A C++ translation unit fixes that underlying type, so an
+ * out-of-range value a caller passes (rejected with OSC_E_FORMAT) is still a value of the type. */
+#ifdef __cplusplus
+#define OSC_ENUM(name) enum name : int
+#else
+#define OSC_ENUM(name) enum name
+#endif
+
+typedef OSC_ENUM(osc_status_e) {
   OSC_OK = 0,
   OSC_E_NULL = 1,   /* a required pointer is NULL (or a pointer that must be NULL is not) */
   OSC_E_SHAPE = 2,  /* a size or the group size violates the constraints of the call    */
@@ -85,13 +93,13 @@ typedef enum {
   OSC_E_DEVICE = 6  /* the HIP runtime rejected a kernel launch                          */
 } osc_status;
 
-typedef enum {
+typedef OSC_ENUM(osc_fmt_e) {
   OSC_MXFP4 = 0, /* E2M1 elements + E8M0 group scale */
   OSC_MXFP8 = 1, /* E4M3 elements + E8M0 group scale */
   OSC_FP6P = 2   /* G = 16 pairs: E3M2 elements + one E8M0 scale per two 16-groups (below) */
 } osc_fmt;
 
-typedef enum {
+typedef OSC_ENUM(osc_ytype_e) {
   OSC_Y_BF16 = 0, /* output rounded to bfloat16 (nearest, ties to even) */
   OSC_Y_F32 = 1   /* output kept in fp32 */
 } osc_ytype;
@@ -103,7 +111,9 @@ typedef enum {
  * osc_pack_weights -- offline weight preparation (§3.2 weight side, §3.3).
  *   W   [N][H] bf16, device.  Quantized unmodified along H in groups of G.
  *   L   host int32[K] table slice, or NULL (no compensation path: WL must be NULL).
- *   wfmt  OSC_MXFP4, OSC_MXFP8, or OSC_FP6P (G = 16).
+ *   wfmt  OSC_MXFP4, OSC_MXFP8, or OSC_FP6P (G = 16).  OSC_MXFP8 weights serve only
+ *       the FP8 fallback (§4), which has no compensation path: with L != NULL the
+ *       call returns OSC_E_FORMAT.
  *   QW  element codes, tiled (R = N), device, written.
  *   SW  E8M0 scales, tiled (R = N), device, written.
  *   WL  bf16, tiled (R = N), device, written: WL(n, k) = W[n][k*G + L[k]], or +0
@@ -119,7 +129,9 @@ osc_status osc_pack_weights(const void* W, int N, int H, int G, const int32_t* L
  *   X   [S][H] bf16, device, read only (zeroing is logical).
  *   L   host int32[K] table slice, or NULL: no extraction (direct MX quantization,
  *       and the FP8 fallback of §4); then B must be NULL.
- *   afmt  OSC_MXFP4, OSC_MXFP8, or OSC_FP6P (G = 16).
+ *   afmt  OSC_MXFP4, OSC_MXFP8, or OSC_FP6P (G = 16).  OSC_MXFP8 is the FP8 fallback
+ *       of §4, which extracts nothing: with L != NULL the call returns OSC_E_FORMAT
+ *       (osc_gemm_fp8 takes no B, so the split channels would be lost).
  *   QX  element codes, tiled (R = S), device, written.
  *   SX  E8M0 scales, tiled (R = S), device, written; computed on the zeroed group.
  *   B   bf16, tiled (R = S), device, written: B(s, k) = X[s][k*G + L[k]] bit for
@@ -265,7 +277,8 @@ osc_status osc_linear_decode(const void* X, int S, int H, int G, const int32_t* 
  *       the degree-6 Taylor polynomial of e^r in Horner form with fused
  *       multiply-adds, times 2^n; x > 88 gives +inf and x < -86 gives 0.
  *   L, m, afmt, QX, SX, B  as osc_quant_act_multi with H = F: the tiled W2
- *       activation operand (codes, scales and, with a table, B).
+ *       activation operand (codes, scales and, with a table, B); OSC_MXFP8 with a
+ *       table returns OSC_E_FORMAT there and here.
  * Constraints: as osc_quant_act_multi with H = F, plus S * 2F < 2^34.
  */
 osc_status osc_swiglu_quant(const void* GU, int S, int F, int G, const int32_t* L, int m, osc_fmt afmt,

@@ -27,9 +27,13 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        # OSC_ORACLE_LIBRARY names another build of osc_oracle.c (the sanitizer build of the tests)
+        path = os.environ.get("OSC_ORACLE_LIBRARY")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i = ctypes.c_int
         L.orc_bf16_value.argtypes = [ctypes.c_uint16]

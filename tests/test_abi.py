@@ -81,6 +81,23 @@ def test_pack_weights_validation():
     assert p(l=bp) == 3
 
 
+def test_fp8_fallback_refuses_a_table():
+    """The FP8 fallback (§4) extracts nothing and osc_gemm_fp8 takes no B / W_L: a table with
+    OSC_MXFP8 would zero channels that no later call adds back, so it is refused up front."""
+    keep, lp = L8([-1] * 8)  # even an all -1 table: the combination itself is refused
+    two, tp = L8([0, 5] * 8)
+    qa = lambda l, B, m=1: status("osc_quant_act_multi", A, 16, 256, 32, l, m, 1, A, A, B, None)
+    assert qa(lp, A) == 5 and qa(tp, A, m=2) == 5
+    assert status("osc_quant_act", A, 16, 256, 32, lp, 1, A, A, A, None) == 5
+    assert status("osc_quant_act", A, 0, 256, 32, lp, 1, A, A, A, None) == 5  # even with nothing to do
+    pw = lambda l, WL, m=1: status("osc_pack_weights_multi", A, 64, 256, 32, l, m, 1, A, A, WL, None)
+    assert pw(lp, A) == 5 and pw(tp, A, m=2) == 5
+    assert status("osc_pack_weights", A, 64, 256, 32, lp, 1, A, A, A, None) == 5
+    # the same formats without a table are valid up to the pointer checks
+    assert status("osc_quant_act", U, 16, 256, 32, None, 1, A, A, None, None) == 4
+    assert status("osc_pack_weights", U, 64, 256, 32, None, 1, A, A, None, None) == 4
+
+
 def test_gemm_validation():
     g = lambda QX=A, SX=A, B=A, QW=A, SW=A, WL=A, S=16, N=128, H=256, G=32, Y=A, yt=0: status(
         "osc_gemm", QX, SX, B, QW, SW, WL, S, N, H, G, Y, yt, None)
@@ -140,9 +157,11 @@ def test_multi_validation():
 
 def test_swiglu_quant_validation():
     keep, lp = L8([-1] * 16)  # F=512, G=32: K=16
-    q = lambda GU=A, S=16, F=512, G=32, l=lp, m=1, f=1, QX=A, SX=A, B=A: status(
+    q = lambda GU=A, S=16, F=512, G=32, l=lp, m=1, f=0, QX=A, SX=A, B=A: status(
         "osc_swiglu_quant", GU, S, F, G, l, m, f, QX, SX, B, None)
     assert q(f=5) == 5                       # bad format
+    assert q(f=1) == 5 and q(f=1, m=2, l=L8([-1] * 32)[1]) == 5  # FP8 fallback with a table
+    assert q(f=1, l=None, B=None, GU=U) == 4  # FP8 without a table passes the format check
     assert q(F=384) == 2                     # tiled layout: F % 256
     assert q(G=8) == 2
     assert q(m=0) == 2 and q(m=4) == 2

@@ -43,10 +43,11 @@ def test_swiglu_h_bit_exact_over_every_gate_pattern(up):
     np.testing.assert_array_equal(host_bits16(Hd), oracle.swiglu(GU))
 
 
-@pytest.mark.parametrize("fmt", [osc.OSC_MXFP8, osc.OSC_MXFP4])
+@pytest.mark.parametrize("fmt", [osc.OSC_MXFP4])
 def test_swiglu_quant_h_inside_the_fused_kernel(fmt):
     """The fused kernel's h, seen through the compensation buffer: listing three channels per group
-    copies h there bit for bit; eleven tables cover every channel of every gate pattern."""
+    copies h there bit for bit; eleven tables cover every channel of every gate pattern.  (Only the
+    4-bit path takes a table; the E4M3 codes of h are checked without one below.)"""
     g = all_gate_patterns()
     S, F = g.shape
     G, m = 32, 3
@@ -69,6 +70,20 @@ def test_swiglu_quant_h_inside_the_fused_kernel(fmt):
                 np.testing.assert_array_equal(got_b[:, e::m], href[:, c0 + e::G])
 
 
+def test_swiglu_quant_e4m3_over_every_gate_pattern():
+    """The FP8 fallback's input (no table): E4M3 codes and scales of h over every finite gate pattern."""
+    g = all_gate_patterns()
+    S, F = g.shape
+    u = to_bf16_bits(np.clip(np.random.default_rng(11).normal(0, 0.6, (S, F)), -1, 1))
+    GU = np.concatenate([g, u], axis=1)
+    for G in (32, 64):
+        QX, SX, _ = swiglu_quant(dev_bits16(GU), S, F, G, None, 1, osc.OSC_MXFP8)
+        torch.cuda.synchronize()
+        rq, rs, _ = oracle.swiglu_quant(GU, G, None, 1, oracle.MXFP8)
+        np.testing.assert_array_equal(codes_rm(QX, S, F, osc.OSC_MXFP8), rq)
+        np.testing.assert_array_equal(scales_rm(SX, S, F, G), rs)
+
+
 @pytest.mark.parametrize("G", [16, 32, 64])
 @pytest.mark.parametrize("fmt", [osc.OSC_MXFP4, osc.OSC_MXFP8])
 @pytest.mark.parametrize("m", [0, 1, 2])
@@ -83,6 +98,12 @@ def test_swiglu_quant_ragged_rows(G, fmt, m):
             L[k] = rng.choice(G, size=m, replace=False)
             if rng.random() < 0.2:
                 L[k, -1] = -1
+    if m and fmt == osc.OSC_MXFP8:
+        # the FP8 fallback extracts nothing (no B / W_L in its GEMM): a table is refused
+        with pytest.raises(osc.OscError) as e:
+            swiglu_quant(dev_bits16(GU), S, F, G, L, m, fmt)
+        assert e.value.status == 5  # OSC_E_FORMAT
+        return
     QX, SX, B = swiglu_quant(dev_bits16(GU), S, F, G, L, max(m, 1), fmt)
     torch.cuda.synchronize()
     rq, rs, rb = oracle.swiglu_quant(GU, G, L, max(m, 1), fmt)

@@ -70,3 +70,28 @@ def test_alpha_monotone():
         if prev is not None:
             assert prot <= prev
         prev = prot
+
+
+def test_in_row_ties_and_the_alpha_boundary_m1():
+    """Hand-built groups (tests/calib_cases.py, values exact in bf16 and fp64): two or three channels
+    sharing the row's max |x| give the event to the lowest of them; a max exactly equal to alpha times
+    the group mean is not an event, one just above it is.  Taking the last arg-max, or testing with
+    '>=', fails here."""
+    import calib_cases as cc
+    R = 64
+    L, hits, events = oracle.build_table(to_bf16_bits(cc.calibration_rows(R)), cc.G, cc.ALPHA, cc.RHO)
+    np.testing.assert_array_equal(L, cc.expected(1))
+    np.testing.assert_array_equal(events, cc.expected_events(R))
+    np.testing.assert_array_equal(hits, cc.expected_events(R))  # one channel takes every event
+
+
+def test_in_row_ties_and_the_alpha_boundary_m2():
+    """The same groups with two entries per group: the two largest |x| taken lower channel first among
+    equals (a three-way tie keeps the two lowest), each an event only strictly above alpha * mean."""
+    import calib_cases as cc
+    R = 64
+    L, hits, events = oracle.build_table_multi(to_bf16_bits(cc.calibration_rows(R)), cc.G, 2, cc.ALPHA, cc.RHO)
+    np.testing.assert_array_equal(L, cc.expected(2))
+    np.testing.assert_array_equal(events, cc.expected_events(R))
+    # every listed channel is the event channel on all R rows
+    np.testing.assert_array_equal(hits[L >= 0], R)

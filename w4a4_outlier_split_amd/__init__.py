@@ -22,7 +22,8 @@ import numpy as np
 import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_build", "libosc.so")
+# OSC_LIBRARY names another build of the same library (the host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("OSC_LIBRARY") or os.path.join(_HERE, "_build", "libosc.so")
 
 OSC_MXFP4 = 0
 OSC_MXFP8 = 1

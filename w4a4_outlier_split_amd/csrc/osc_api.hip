@@ -49,6 +49,11 @@ bool valid_fmt(osc_fmt f, int G) { return f == OSC_MXFP4 || f == OSC_MXFP8 || (f
 
 bool valid_m(int m) { return m >= 1 && m <= osc::kMaxChannels; }
 
+// The FP8 fallback (§4) keeps every channel in the microscaled operand: no extraction and no
+// compensation path (osc_gemm_fp8 takes neither B nor W_L), so a table with MXFP8 is refused
+// rather than having its channels zeroed and then dropped.
+bool fmt_takes_table(osc_fmt f, const int32_t* L) { return !(f == OSC_MXFP8 && L != nullptr); }
+
 // the HIP error behind the calling thread's most recent OSC_E_DEVICE
 thread_local hipError_t g_last_error = hipSuccess;
 
@@ -81,7 +86,7 @@ const char* osc_last_device_error(void) {
 
 osc_status osc_quant_act_multi(const void* X, int S, int H, int G, const int32_t* L, int m, osc_fmt afmt, void* QX,
                                uint8_t* SX, void* B, void* stream) {
-  if (!valid_fmt(afmt, G)) return OSC_E_FORMAT;
+  if (!valid_fmt(afmt, G) || !fmt_takes_table(afmt, L)) return OSC_E_FORMAT;
   osc_status st = check_tiled(S, H, G);
   if (st != OSC_OK) return st;
   if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
@@ -114,7 +119,7 @@ osc_status osc_swiglu(const void* GU, int S, int F, void* Hout, void* stream) {
 
 osc_status osc_swiglu_quant(const void* GU, int S, int F, int G, const int32_t* L, int m, osc_fmt afmt, void* QX,
                             uint8_t* SX, void* B, void* stream) {
-  if (!valid_fmt(afmt, G)) return OSC_E_FORMAT;
+  if (!valid_fmt(afmt, G) || !fmt_takes_table(afmt, L)) return OSC_E_FORMAT;
   osc_status st = check_tiled(S, F, G);
   if (st != OSC_OK) return st;
   if ((long long)S * (F / 4) > 0x7FFFFFFFLL) return OSC_E_SHAPE;  // the input rows are 2F wide
@@ -134,7 +139,7 @@ osc_status osc_swiglu_quant(const void* GU, int S, int F, int G, const int32_t* 
 
 osc_status osc_pack_weights_multi(const void* W, int N, int H, int G, const int32_t* L, int m, osc_fmt wfmt, void* QW,
                                   uint8_t* SW, void* WL, void* stream) {
-  if (!valid_fmt(wfmt, G)) return OSC_E_FORMAT;
+  if (!valid_fmt(wfmt, G) || !fmt_takes_table(wfmt, L)) return OSC_E_FORMAT;
   osc_status st = check_tiled(N, H, G);
   if (st != OSC_OK) return st;
   if (!valid_m(m) || (H / G) * m > OSC_MAX_GROUPS) return OSC_E_SHAPE;
