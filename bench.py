@@ -750,11 +750,11 @@ def main():
     if os.path.exists(tf_path):
         with open(tf_path) as f:
             tf = json.load(f)
-        if tf.get("source_hash") == src_hash("osc_gemm.hip"):
+        if tf.get("source_hash") == src_hash("osc_gemm_mx4.hip", "osc_device.h"):
             traffic = tf.get("bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["mxfp4"], "unit": "TFLOP/s",
                 "frac": achieved / PEAK_TFLOPS["mxfp4"], "traffic": traffic,
-                "kernel": "k_gemm (osc_gemm, MXFP4 scaled MFMA + fused bf16 compensation)",
+                "kernel": "k_gemm_mx4 (osc_gemm_mx4, MXFP4 scaled MFMA + fused bf16 compensation)",
                 "flops_per_launch": gemm_flops, "avg_launch_us": head["t_gemm_us"]}
     sclk = head.get("sclk_mhz")
     if sclk:

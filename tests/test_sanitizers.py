@@ -37,7 +37,7 @@ def run_child(tests, preload, extra_env, tmp_path):
 
 
 def test_host_validation_under_sanitizers(tmp_path):
-    objs = [os.path.join(PKG_BUILD, f) for f in ("osc_quant.o", "osc_gemm.o", "osc_gemm_dec.o")]
+    objs = [os.path.join(PKG_BUILD, f) for f in ("osc_quant.o", "osc_gemm.o", "osc_gemm_mx4.o", "osc_gemm_dec.o")]
     if not os.path.exists(HIPCC) or not all(os.path.exists(o) for o in objs):
         pytest.skip("needs hipcc and the library's objects (python w4a4_outlier_split_amd/build.py)")
     rt = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libosc.so")
-SOURCES = ["osc_api.hip", "osc_quant.hip", "osc_gemm.hip", "osc_gemm_dec.hip"]
+SOURCES = ["osc_api.hip", "osc_quant.hip", "osc_gemm.hip", "osc_gemm_mx4.hip", "osc_gemm_dec.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

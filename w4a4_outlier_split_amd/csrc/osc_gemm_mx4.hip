@@ -1,0 +1,480 @@
+// Dual-path OSC GEMM for MXFP4 activations and weights at G = 32 / 64 (OSC page
+// "W4A4量化技术：OSC框架如何实现高效LLM部署", §3.2: Y = (Q_X ⊗ Q_W)·S + B·W_L; §3.3: the 4-bit and
+// the 16-bit operand streams are consumed by one kernel into the same accumulators).
+//
+// Swapped operands.  The weight fragment is the MFMA's A operand and the activation fragment its B
+// operand, so each 32x32 accumulator block is a block of Yᵀ: lane l holds output row (token) l % 32
+// and, in registers 4g .. 4g+3, the 4 consecutive output columns 8g + 4 (l / 32) + [0, 4).  The
+// epilogue packs those 4 values into 8 contiguous bytes of a Y row with two conversions.
+//
+// Pipeline (per workgroup: a BM x BN tile of Y, WAVES_M x WAVES_N wavefronts, each a WTM x WTN
+// sub-tile = TM x TN blocks).  K is cut into stages: first ceil(KC / 32) compensation stages
+// (32 columns of B / W_L, bf16: v_mfma_f32_32x32x16_bf16), then H / 128 main stages (128 E2M1
+// codes: v_mfma_scale_f32_32x32x64_f8f6f4), each one 64-byte row per operand row, copied
+// global -> LDS by LDS-DMA into a ring of NS buffers, NS - 1 stages ahead.  One barrier per stage
+// splits it into its two K halves: half 0 before the barrier, half 1 after it, while the next
+// stage's first-half fragments and scales are read; compensation and main stages share that
+// schedule.  A stage's loads (row blocks and the two sides' scale dwords) are dealt out to all
+// waves alike, the slots left over going through a resource with no records, and past the last
+// stage every wave keeps issuing such loads: the stage body has no branch and every wait is the
+// same count.
+#include <type_traits>
+
+#include "osc_device.h"
+#include "osc_internal.h"
+
+namespace osc {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int roundup(int x, int m) { return (x + m - 1) / m * m; }
+
+template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+struct Cfg4 {
+  static constexpr int NW = WAVES_M * WAVES_N;  // wavefronts per workgroup
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 blocks per wavefront
+  // The loads of one stage, each one LDS-DMA of 64 lanes x 16 bytes: XB blocks of 16 activation
+  // rows (64 bytes each), WB blocks of 16 weight rows, the activation scale dwords of the tile (4
+  // rows per lane), the weight scale dwords.  Load g of the stage is issued by wave g % NW; every
+  // wave issues D of them, the slots past the last load going through a resource with no records
+  // into a spare kilobyte of the stage.
+  static constexpr int XB = BM / 16, WB = BN / 16;
+  static constexpr int NLOAD = XB + WB + 2;
+  static constexpr int D = (NLOAD + NW - 1) / NW;  // loads per wave per stage
+  enum { kXRows = 0, kWRows = 1, kXScale = 2, kWScale = 3, kNone = 4 };
+  static constexpr int kind(int g) {
+    return g < XB ? kXRows : g < XB + WB ? kWRows : g == XB + WB ? kXScale : g == XB + WB + 1 ? kWScale : kNone;
+  }
+  // the kind of slot i when it is the same for every wave, else -1
+  static constexpr int slot_kind(int i) {
+    const int k = kind(NW * i);
+    for (int w = 1; w < NW; ++w)
+      if (kind(NW * i + w) != k) return -1;
+    return k;
+  }
+  static constexpr int OFF_B = BM * 64;               // weight rows
+  static constexpr int OFF_SA = (BM + BN) * 64;       // activation scale dwords (one per row)
+  static constexpr int OFF_SB = OFF_SA + 1024;        // weight scale dwords
+  static constexpr int OFF_J = OFF_SB + 1024;         // spare kilobyte (the empty loads)
+  static constexpr int STAGE = OFF_J + 1024;
+  static constexpr int NS = (160 * 1024) / STAGE > 4 ? 4 : (160 * 1024) / STAGE;
+  // LDS row stride of the bf16 output image: 8 bytes more than a row, so the 8-byte writes of 32
+  // consecutive rows fall on 32 distinct bank pairs
+  static constexpr int YS = 2 * BN + 8;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(BM <= 256 && BN <= 256, "one scale load per operand side");
+  static_assert(NS >= 3, "the LDS ring must hold at least 3 stages");
+  static_assert(D * (NS - 2) < 64, "vmcnt range");
+  static_assert(BM * YS <= NS * STAGE, "the output image must fit in the LDS ring");
+  static_assert(G == 32 || G == 64, "scale bytes per stage");
+};
+
+template <int G, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
+    const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX, const uint8_t* __restrict__ Bc,
+    const uint8_t* __restrict__ QW, const uint8_t* __restrict__ SW, const uint8_t* __restrict__ WL,
+    void* __restrict__ Y, int S, int N, int H, int KC) {
+  using C = Cfg4<G, BM, BN, WAVES_M, WAVES_N>;
+  constexpr int NS = C::NS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * C::STAGE];
+  lds_u8* const smem = (lds_u8*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+
+  // XCD-aware tile order: consecutive workgroups go to different XCDs; each XCD gets a contiguous
+  // run of tiles (M fastest) so the tiles sharing a weight panel share that XCD's L2.
+  const int ntm = (S + BM - 1) / BM;
+  const int ntn = (N + BN - 1) / BN;
+  const int total = ntm * ntn;
+  int tile = blockIdx.x;
+  if ((total & 7) == 0) tile = (tile & 7) * (total >> 3) + (tile >> 3);
+  const int m0 = (tile % ntm) * BM;
+  const int n0 = (tile / ntm) * BN;
+
+  const int nks = H / 128;
+  const int ncs = COMP ? (KC + 31) / 32 : 0;
+  const int nst = ncs + nks;
+
+  // ------------------------------------------------------------ DMA sources (fixed per lane)
+  // All operands arrive in the tiled layout (a stage of a tile is one R-major block per panel), so
+  // a load's address is its panel base (scalar) plus the lane's fixed 32-bit offset.  Row block b
+  // fills LDS chunks [64b, 64b+64) of its region; lane l fills chunk p = 64b + l with the logical
+  // chunk that the swizzle puts there.  Rows past the ragged edge are clamped (never stored); scale
+  // dwords past it lie outside the panel's resource and arrive as zeros.
+  int kind[C::D], dst[C::D], ccol[C::D];  // ccol: first compensation column of the lane's chunk
+  uint32_t voff[C::D];
+#pragma unroll
+  for (int i = 0; i < C::D; ++i) {
+    const int g = C::NW * i + wave;
+    const int k = C::slot_kind(i) >= 0 ? C::slot_kind(i) : C::kind(g);
+    kind[i] = k;
+    const bool xs = k == C::kXRows || k == C::kXScale;
+    const int r0 = xs ? m0 : n0, rmax = (xs ? S : N) - 1;
+    if (k == C::kXRows || k == C::kWRows) {
+      const int blk = k == C::kXRows ? g : g - C::XB;
+      const int p = blk * 64 + lane;
+      const int r = p >> 2;
+      const int cc = swz<64>(r, p & 3);
+      voff[i] = (uint32_t)min(r0 + r, rmax) * 64u + (uint32_t)(cc * 16);
+      ccol[i] = 8 * cc;
+      dst[i] = (k == C::kXRows ? 0 : C::OFF_B) + blk * 1024;
+    } else if (k == C::kXScale || k == C::kWScale) {
+      voff[i] = (uint32_t)(r0 + 4 * lane) * 4u;
+      dst[i] = k == C::kXScale ? C::OFF_SA : C::OFF_SB;
+      ccol[i] = 0;
+    } else {
+      voff[i] = 0;
+      dst[i] = C::OFF_J;
+      ccol[i] = 0;
+    }
+  }
+
+  // The loads of stage s.  Stage s is a compensation panel for s < ncs (its scale loads copy scale
+  // panel 0, unused), else code panel s - ncs.  Past the last stage the ring keeps issuing the same
+  // loads through resources with no records: they return zeros without touching memory (into a
+  // buffer no later stage reads), so every stage has the same loads in flight and the same waits.
+  const auto null_rsrc = panel_rsrc(QX, 0);
+  // MC: stage s may be a compensation stage (false: s >= ncs is known)
+  auto issue = [&](auto mc_t, int s, lds_u8* __restrict__ buf) {
+    constexpr bool MC = decltype(mc_t)::value;
+    const bool live = s < nst;
+    const bool comp = COMP && MC && s < ncs;
+    // panel indices (0 past the last stage, whose loads touch nothing) and bases as plain
+    // integers, so that every choice stays a scalar select rather than a branch
+    const int kp = live ? (comp ? s : s - ncs) : 0;
+    const int sp = live && !comp ? (G == 64 ? (s - ncs) >> 1 : s - ncs) : 0;
+    const uintptr_t bx = (uintptr_t)((comp ? Bc : QX) + (long)kp * (S * 64));
+    const uintptr_t bw = (uintptr_t)((comp ? WL : QW) + (long)kp * (N * 64));
+    const uintptr_t bxs = (uintptr_t)(SX + (long)sp * (S * 4));
+    const uintptr_t bws = (uintptr_t)(SW + (long)sp * (N * 4));
+    const int nx = live ? S * 64 : 0, nw = live ? N * 64 : 0;
+    const int nxs = live ? S * 4 : 0, nws = live ? N * 4 : 0;
+    // compensation columns past KC (the padding of the last panel) are loaded from outside the
+    // resource, as zeros
+    const int climit = comp ? KC - 32 * s : 32;
+#pragma unroll
+    for (int i = 0; i < C::D; ++i) {
+      uintptr_t b;
+      int n;
+      const int sk = C::slot_kind(i);
+      if (sk == C::kXRows) {
+        b = bx, n = nx;
+      } else if (sk == C::kWRows) {
+        b = bw, n = nw;
+      } else {
+        const int k = kind[i];
+        b = k == C::kXRows ? bx : bw;
+        n = k == C::kXRows ? nx : nw;
+        b = k == C::kXScale ? bxs : b;
+        n = k == C::kXScale ? nxs : n;
+        b = k == C::kWScale ? bws : b;
+        n = k == C::kWScale ? nws : n;
+        n = k == C::kNone ? 0 : n;
+      }
+      const uint32_t off = COMP && MC && ccol[i] >= climit ? 0x80000000u : voff[i];
+      dma16(panel_rsrc((const uint8_t*)b, n), off, buf + dst[i]);
+    }
+  };
+
+  v16f acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // prologue: the first NS - 1 stages in flight
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(std::true_type{}, s, smem + s * C::STAGE);
+
+  // ------------------------------------------------------------ fragments
+  // K half m of a stage: lane l reads row (block base + l % 32), 16-byte chunk 2m + l / 32 (E2M1:
+  // K [64m + 32 h, +32) of the stage; bf16: columns [16m + 8h, +8) of the compensation panel).
+  // Block bases are multiples of 32, so the swizzled chunk depends on the lane only.
+  const int lrow = lane & 31;
+  const int h = lane >> 5;
+  const int loff0 = lrow * 64 + (swz<64>(lrow, h) << 4);
+  const int loff1 = lrow * 64 + (swz<64>(lrow, 2 + h) << 4);
+  struct Frag {  // one K half of a stage: TM activation and TN weight fragments
+    v4i x[C::TM], w[C::TN];
+  };
+  struct Scales {  // a stage's scale dwords, shifted so that byte opsel of the MFMA is the lane's
+    uint32_t x[C::TM], w[C::TN];
+  };
+  auto lds4 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v4i*)p; };
+  auto lds32 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) uint32_t*)p; };
+  auto read_half = [&](int st, int m, Frag& f) {
+    const lds_u8* As = smem + (st % NS) * C::STAGE;
+    const lds_u8* Bs = As + C::OFF_B;
+    const int lo = m ? loff1 : loff0;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) f.x[i] = lds4(As + (wm * C::WTM + 32 * i) * 64 + lo);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) f.w[j] = lds4(Bs + (wn * C::WTN + 32 * j) * 64 + lo);
+  };
+  // raw scale dwords of stage st (row l % 32 of each block)
+  auto read_scales = [&](int st, Scales& sr) {
+    const lds_u8* SAs = smem + (st % NS) * C::STAGE + C::OFF_SA;
+    const lds_u8* SBs = smem + (st % NS) * C::STAGE + C::OFF_SB;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) sr.x[i] = lds32(SAs + (wm * C::WTM + 32 * i + lrow) * 4);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) sr.w[j] = lds32(SBs + (wn * C::WTN + 32 * j + lrow) * 4);
+  };
+  // G = 32: the stage's four bytes are 32-blocks 0..3, lane half h supplies block 2m + h: shift by
+  // 8h, then opsel 2m.  G = 64: group m of the stage for both lane halves, in the half of the dword
+  // that belongs to this stage (two stages share a scale dword): shift by 16 (stage parity), opsel m.
+  auto shift_scales = [&](int st, const Scales& sr, Scales& sc) {
+    const uint32_t sh = G == 32 ? 8u * (uint32_t)h : 16u * (uint32_t)((st - ncs) & 1);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) sc.x[i] = sr.x[i] >> sh;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) sc.w[j] = sr.w[j] >> sh;
+  };
+  auto mma = [&](int m, const Frag& f, const Scales& sc, bool comp) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        if (COMP && comp)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, f.w[j]),
+                                                              __builtin_bit_cast(v8bf, f.x[i]), acc[i][j], 0, 0, 0);
+        else if (G == 32 && m == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), widen(f.x[i]), acc[i][j], kFp4,
+                                                                      kFp4, 0, sc.w[j], 0, sc.x[i]);
+        else if (G == 32)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), widen(f.x[i]), acc[i][j], kFp4,
+                                                                      kFp4, 2, sc.w[j], 2, sc.x[i]);
+        else if (m == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), widen(f.x[i]), acc[i][j], kFp4,
+                                                                      kFp4, 0, sc.w[j], 0, sc.x[i]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), widen(f.x[i]), acc[i][j], kFp4,
+                                                                      kFp4, 1, sc.w[j], 1, sc.x[i]);
+      }
+  };
+  constexpr int NM_H = C::TM * C::TN;   // MFMAs per half-stage
+  constexpr int NF = C::TM + C::TN;     // fragment (or scale) reads per half-stage
+  // One stage st (not the last): f0 holds its first half's fragments, sc its scales.
+  //   top    issue the DMA of stage st + NS - 1, read the second half's fragments of stage st;
+  //   half 0 MFMAs on f0;
+  //   middle wait for this wave's loads of stage st + 1 and barrier: stage st + 1 is visible to
+  //          all, and no wave reads stage st - 1 any more (the next iteration's DMA refills it);
+  //   half 1 MFMAs on f1 while stage st + 1's scales and first-half fragments are read.
+  // CS: stage st is a compensation stage; NCS: so is stage st + 1.
+  Frag f0, f1;
+  Scales sc, sr;
+  // iss(s, buf): the loads of stage s into ring buffer buf
+  auto stage = [&](auto cs_t, auto ncs_t, int st, auto&& iss) {
+    constexpr bool CS = decltype(cs_t)::value, NCS = decltype(ncs_t)::value;
+    iss(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE);
+    read_half(st, 1, f1);
+    mma(0, f0, sc, CS);
+    Interleave<0, NM_H, C::D, NF>::run();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<(NS - 2) * C::D>();
+    lds_barrier();
+    if constexpr (!NCS) read_scales(st + 1, sr);
+    read_half(st + 1, 0, f0);
+    mma(1, f1, sc, CS);
+    Interleave<0, NM_H, 0, NCS ? NF : 2 * NF>::run();
+    if constexpr (!NCS) shift_scales(st + 1, sr, sc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto iss_comp = [&](int s, lds_u8* buf) { issue(T{}, s, buf); };
+  auto iss_main = [&](int s, lds_u8* buf) { issue(F{}, s, buf); };
+
+  wait_vm<(NS - 2) * C::D>();  // stage 0 complete for this wave
+  lds_barrier();
+  const bool comp0 = COMP && ncs > 0;
+  read_half(0, 0, f0);
+  if (!comp0) {
+    read_scales(0, sr);
+    shift_scales(0, sr, sc);
+  }
+  int st = 0;
+  if constexpr (COMP) {
+    for (; st + 1 < ncs; ++st) stage(T{}, T{}, st, iss_comp);
+    if (st < ncs) {  // the last compensation stage hands over to the first main stage
+      stage(T{}, F{}, st, iss_comp);
+      ++st;
+    }
+  }
+  // Main stages whose loads exist: each load slot keeps its own running panel pointer, advanced by
+  // a fixed stride per stage (the scale panels of G = 64 advance every other stage), so a stage
+  // costs a few scalar adds instead of recomputing every base.
+  if (st + NS - 1 < nst) {
+    const int s0 = st + NS - 1;  // the first stage these iterations load (a main stage)
+    const int k0 = s0 - ncs;
+    uintptr_t fp[C::D];
+    int fn[C::D];
+    uint32_t fsa[C::D], fsb[C::D];  // strides after even / odd positions of the pair loop
+#pragma unroll
+    for (int i = 0; i < C::D; ++i) {
+      const int k = kind[i];
+      const bool odd0 = (k0 & 1) != 0;  // G = 64: a scale panel ends after an odd stage
+      uintptr_t b;
+      int n;
+      uint32_t sa, sb;
+      if (k == C::kXRows || k == C::kWRows) {
+        const int R = k == C::kXRows ? S : N;
+        b = (uintptr_t)((k == C::kXRows ? QX : QW) + (long)k0 * (R * 64));
+        n = R * 64;
+        sa = sb = (uint32_t)(R * 64);
+      } else if (k == C::kXScale || k == C::kWScale) {
+        const int R = k == C::kXScale ? S : N;
+        b = (uintptr_t)((k == C::kXScale ? SX : SW) + (long)(G == 64 ? k0 >> 1 : k0) * (R * 4));
+        n = R * 4;
+        sa = G == 32 || odd0 ? (uint32_t)(R * 4) : 0u;
+        sb = G == 32 || !odd0 ? (uint32_t)(R * 4) : 0u;
+      } else {
+        b = (uintptr_t)QX;
+        n = 0;
+        sa = sb = 0;
+      }
+      fp[i] = b, fn[i] = n, fsa[i] = sa, fsb[i] = sb;
+    }
+    auto iss_fast = [&](auto odd_t) {
+      return [&](int, lds_u8* buf) {
+#pragma unroll
+        for (int i = 0; i < C::D; ++i) {
+          dma16(panel_rsrc((const uint8_t*)fp[i], fn[i]), voff[i], buf + dst[i]);
+          fp[i] += decltype(odd_t)::value ? fsb[i] : fsa[i];
+        }
+      };
+    };
+    for (; st + NS < nst; st += 2) {
+      stage(F{}, F{}, st, iss_fast(F{}));
+      stage(F{}, F{}, st + 1, iss_fast(T{}));
+    }
+    if (st + NS - 1 < nst) {
+      stage(F{}, F{}, st, iss_fast(F{}));
+      ++st;
+    }
+  }
+  // the last NS - 2 stages before the last one: their loads run past the end (empty resources)
+  for (; st + 1 < nst; ++st) stage(F{}, F{}, st, iss_main);
+  // the last stage: no loads of a next stage, no barrier (the epilogue starts with one)
+  read_half(nst - 1, 1, f1);
+  mma(0, f0, sc, false);
+  mma(1, f1, sc, false);
+  wait_vm<0>();  // the ring's trailing loads have landed before the LDS is reused
+
+  // ---------------------------------------------------------------- epilogue
+  // accumulator block (i, j), registers 4g .. 4g+3: Y[m][n + e] for m = wm*WTM + 32 i + l % 32 and
+  // n = wn*WTN + 32 j + 8 g + 4 (l / 32), e < 4 (tile coordinates)
+  const int mrow = wm * C::WTM + lrow;
+  const int ncol = wn * C::WTN + 4 * h;
+  const bool full = m0 + BM <= S && n0 + BN <= N;
+  if constexpr (YT == OSC_Y_BF16) {
+    if ((N & 7) == 0) {
+      // bf16 through LDS: each lane writes its 4 values as 8 contiguous bytes of a row of the tile
+      // image; then the workgroup reads whole 16-byte row chunks and writes full cache lines
+      lds_barrier();  // no wave reads the ring any more and every DMA has landed
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v16f& a = acc[i][j];
+            const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a[4 * g], a[4 * g + 1]}, v2bf));
+            const uint32_t hi =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a[4 * g + 2], a[4 * g + 3]}, v2bf));
+            *(__attribute__((address_space(3))) v2i*)(smem + (mrow + 32 * i) * C::YS + 2 * (ncol + 32 * j + 8 * g)) =
+                v2i{(int)lo, (int)hi};
+          }
+      lds_barrier();
+      constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+      constexpr int NT = C::NW * 64;
+      static_assert((BM * CPR) % NT == 0, "whole chunks per thread");
+#pragma unroll
+      for (int q = 0; q < BM * CPR / NT; ++q) {
+        const int idx = q * NT + tid;
+        const int row = idx / CPR, cc = idx % CPR;
+        const v4i v = lds4(smem + row * C::YS + 16 * cc);
+        // streaming store: Y is not read again by this kernel
+        if (full || (m0 + row < S && n0 + 8 * cc < N))
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(static_cast<__bf16*>(Y) + (long)(m0 + row) * N + n0 + 8 * cc));
+      }
+      return;
+    }
+  }
+  // fp32 output, or bf16 rows that are not 16-byte aligned: stores straight from the accumulators
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m = m0 + mrow + 32 * i;
+        const int n = n0 + ncol + 32 * j + 8 * g;
+        const v16f& a = acc[i][j];
+        if constexpr (YT == OSC_Y_F32) {
+          if (full && (N & 3) == 0) {
+            __builtin_nontemporal_store(v4f{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]},
+                                        reinterpret_cast<v4f*>(static_cast<float*>(Y) + (long)m * N + n));
+            continue;
+          }
+        }
+        if (m < S) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) {
+              if constexpr (YT == OSC_Y_F32)
+                static_cast<float*>(Y)[(long)m * N + n + e] = a[4 * g + e];
+              else
+                static_cast<__bf16*>(Y)[(long)m * N + n + e] = (__bf16)a[4 * g + e];
+            }
+        }
+      }
+}
+
+template <int G, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
+hipError_t run4(const GemmArgs& a, hipStream_t st) {
+  const int tiles = ((a.S + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_gemm_mx4<G, COMP, YT, BM, BN, WAVES_M, WAVES_N>), dim3(tiles), dim3(WAVES_M * WAVES_N * 64), 0,
+                     st, static_cast<const uint8_t*>(a.QX), a.SX, static_cast<const uint8_t*>(a.B),
+                     static_cast<const uint8_t*>(a.QW), a.SW, static_cast<const uint8_t*>(a.WL), a.Y, a.S, a.N, a.H,
+                     a.kc);
+  return hipGetLastError();
+}
+
+// Tile choice (the MI355X reading of the page's "adaptive resource scheduling", §3.3): the
+// largest tile that still gives (nearly) every one of the 256 CUs a tile, since bigger tiles move
+// fewer operand bytes per product.
+template <int G, bool COMP, int YT>
+hipError_t pick4(const GemmArgs& a, hipStream_t st) {
+  constexpr long kCover = 240;  // tiles that count as covering the 256 CUs
+  auto tiles = [&](int bm, int bn) { return (long)((a.S + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  if (tiles(256, 256) >= kCover) return run4<G, COMP, YT, 256, 256, 4, 2>(a, st);
+  if (a.N % 192 == 0 && tiles(256, 192) >= kCover) return run4<G, COMP, YT, 256, 192, 4, 2>(a, st);
+  if (tiles(256, 128) >= kCover) return run4<G, COMP, YT, 256, 128, 4, 2>(a, st);
+  if (tiles(128, 128) >= kCover) return run4<G, COMP, YT, 128, 128, 4, 2>(a, st);
+  return run4<G, COMP, YT, 64, 64, 2, 2>(a, st);
+}
+
+template <int G>
+hipError_t pick4_comp(const GemmArgs& a, hipStream_t st) {
+  const bool comp = a.B != nullptr;
+  if (a.yt == OSC_Y_F32) return comp ? pick4<G, true, OSC_Y_F32>(a, st) : pick4<G, false, OSC_Y_F32>(a, st);
+  return comp ? pick4<G, true, OSC_Y_BF16>(a, st) : pick4<G, false, OSC_Y_BF16>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mx4(const GemmArgs& a, hipStream_t st) {
+  if (a.S == 0 || a.N == 0) return hipSuccess;
+  return a.G == 32 ? pick4_comp<32>(a, st) : pick4_comp<64>(a, st);
+}
+
+}  // namespace osc
