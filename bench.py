@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=2000, help="untimed steps first (~0.1 s: clocks settle)")
+    p.add_argument("--settle", type=float, default=0.3,
+                   help="before the warmup steps, untimed steps for at least this many seconds: a burst of a "
+                        "millisecond leaves the core and memory clocks at their idle levels")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the extra workload rows")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -162,6 +165,22 @@ def step_gemm(osc, l, s):
                          osc.OSC_Y_BF16, s)
 
 
+SETTLE_S = 0.3
+
+
+def settle(torch, body, seconds):
+    """Untimed repetitions of body() for at least `seconds` of wall time (chunks of 64, each
+    synchronized), so that the timed region starts with the device at its loaded clocks."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(64):
+            body(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def time_layer(torch, osc, sets, steps, warmup, stream):
     """Run quant + GEMM over rotating buffer sets.  The steps run back to back under one event
     pair (the step time); a second pass with an event between the two kernels of every step gives
@@ -172,11 +191,15 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
     quant = lambda l: step_quant(osc, l, s)
     gemm = lambda l: step_gemm(osc, l, s)
 
+    def one(i):
+        l = sets[i % len(sets)]
+        quant(l)
+        gemm(l)
+
     with torch.cuda.stream(stream):
+        settle(torch, one, SETTLE_S)
         for i in range(warmup):
-            l = sets[i % len(sets)]
-            quant(l)
-            gemm(l)
+            one(i)
         ev = TimingEvents(2 * steps + 3)
         gc.collect()
         gc.disable()  # no collector pause inside the timed region
@@ -508,6 +531,7 @@ def run_block(torch, osc, dev, stream, steps, warmup, S=4096):
         calls = [lambda: q.forward(Xq, S, aq, Yq, stream=stream), lambda: o.forward(Xo, S, ao, Yo, stream=stream),
                  lambda: mlp.forward(Xu, S, bufs, Ym, stream=stream)]
         with torch.cuda.stream(stream):
+            settle(torch, lambda _: [c() for c in calls], SETTLE_S)
             for _ in range(warmup):
                 for c in calls:
                     c()
@@ -631,6 +655,8 @@ def main():
     import synth
     import w4a4_outlier_split_amd as osc
 
+    global SETTLE_S
+    SETTLE_S = args.settle
     dev = "cuda:0"
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
@@ -771,7 +797,7 @@ def main():
     ms = head["ms_per_step"]
     out = {
         "metric": "fused OSC W4A4 quant+GEMM TFLOP/s at Qwen3-8B shapes; % of MXFP4 MFMA peak",
-        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_s": args.settle,
         "ms_per_step": ms, "host_ms_per_step": head["host_ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4", "data": "synthetic",
