@@ -310,10 +310,11 @@ def test_gemm_fp8_ragged(S, N, H, G, wfmt):
 
 # ------------------------------------------------------------------ skinny-S (decode) kernel
 
-@pytest.mark.parametrize("S", [1, 17, 32])
+@pytest.mark.parametrize("S", [1, 9, 16, 17, 32])
 @pytest.mark.parametrize("G,comp", [(16, True), (32, True), (32, False), (64, True)])
 def test_gemm_decode_kernel(S, G, comp):
-    """S <= 32 runs the skinny-S kernel (K split over the waves of a 32-column block)."""
+    """S <= 32 runs the skinny-S kernel (K split over the waves of a 32-column block); S = 9 and 16
+    leave rows of the 32-row MFMA blocks unused."""
     N, H = 300, 1536  # ragged last column block; 12 main stages over 8 waves
     X = synth.random_bf16((S, H), seed=S * 7 + G, scale=2.0)
     W = synth.random_bf16((N, H), seed=G + 3, scale=0.05)
