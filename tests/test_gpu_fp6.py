@@ -131,3 +131,80 @@ def test_gemm_fp6p_sweep_workload():
     ref = oracle.gemm_fp6p(rqx, rsx, rqw, rsw, rb, rwl)
     got = Y.index_select(0, torch.from_numpy(rows).to(Y.device)).index_select(1, torch.from_numpy(cols).to(Y.device))
     assert_y_close(got.double().cpu().numpy(), ref, what="fp6p G-sweep S=8192")
+
+
+def _e2m1_values(Q4, H):
+    """uint8[R, H/2] MXFP4 codes (channel 2i in the low nibble of byte i) -> float64[R, H] E2M1 values."""
+    mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    c = np.empty((Q4.shape[0], H), np.uint8)
+    c[:, 0::2] = Q4 & 15
+    c[:, 1::2] = Q4 >> 4
+    return np.where(c & 8, -1.0, 1.0) * mag[c & 7]
+
+
+def _e3m2_values(Q6, H):
+    """uint8[R, 3H/4] packed E3M2 codes -> float64[R, H] values (sign bit 5, exponent bits 4..2 with
+    bias 3, mantissa bits 1..0; exponent 0: multiples of 1/16)."""
+    out = np.empty((Q6.shape[0], H))
+    for k in range(H):
+        c = oracle.get_code6(Q6, k).astype(np.int64)
+        e, m = (c >> 2) & 7, c & 3
+        mag = np.where(e == 0, m / 16.0, (1.0 + m / 4.0) * np.exp2(e - 3.0))
+        out[:, k] = np.where(c & 32, -mag, mag)
+    return out
+
+
+def test_fp6p_changes_only_pairs_more_than_5_scale_codes_apart():
+    """Against the exact G = 16 MXFP4 quantization (the oracle at G = 16): the GPU's E3M2 pairs carry
+    every element exactly in pairs whose two scale codes differ by at most 5, and the larger group of
+    every pair exactly; in pairs further apart the smaller group's elements move by at most half an
+    E3M2 step (1/32 of the pair scale), and on these rows (gaps up to 9) some do move.  Y of the pair
+    GEMM differs from Y of the exact G = 16 layer by no more than those moves can make it."""
+    S, H, N = 48, 1024, 96
+    rng = np.random.default_rng(77)
+    X = crafted_rows(rng, S, H)
+    W = synth.random_bf16((N, H), seed=78, scale=0.05)
+    QX, SX, _ = _quant_plain(dev_bits16(X), S, H)
+    from gpu_util import _tiled_outputs
+    QW, SW, _ = _tiled_outputs(N, H, 16, FP6P, False)
+    osc.osc_pack_weights(dev_bits16(W), N, H, 16, None, FP6P, QW, SW, None)
+    Y = gemm_fp6p(QX, SX, None, QW, SW, None, S, N, H, 1)
+    torch.cuda.synchronize()
+
+    def pair_values(Q6, S32, R):
+        return _e3m2_values(Q6, H) * np.exp2(np.repeat(S32.astype(np.float64) - 127.0, 32, axis=1))
+
+    def exact_values(A, R):
+        q4, s16, _ = oracle.quant_act(A, 16, None)
+        return _e2m1_values(q4, H) * np.exp2(np.repeat(s16.astype(np.float64) - 127.0, 16, axis=1)), s16
+
+    got_x = pair_values(codes6_rm(QX, S, H), scales_rm(SX, S, H, 32), S)
+    ex_x, s16 = exact_values(X, S)
+    s = s16.astype(int)
+    gap = np.abs(s[:, 0::2] - s[:, 1::2])                                   # [S, H/32]
+    small = np.where(s[:, 0::2] < s[:, 1::2], 0, 1)                         # which 16-group is smaller
+    E = np.maximum(np.maximum(s[:, 0::2], s[:, 1::2]) - 2, 0)
+    d = got_x - ex_x
+    for b in range(H // 32):
+        blk = slice(32 * b, 32 * b + 32)
+        near = gap[:, b] <= 5
+        assert np.all(d[near, blk] == 0.0), f"pair {b}: a pair within 5 scale codes changed"
+        for g in (0, 1):
+            grp = slice(32 * b + 16 * g, 32 * b + 16 * g + 16)
+            bigger = ~near & (small[:, b] != g)
+            assert np.all(d[bigger, grp] == 0.0), f"pair {b}: the larger group changed"
+            smaller = ~near & (small[:, b] == g)
+            half_step = np.exp2(E[smaller, b] - 127.0 - 5.0)[:, None]
+            assert np.all(np.abs(d[smaller, grp]) <= half_step), f"pair {b}: moved by more than half a step"
+    assert np.count_nonzero(d) > 0 and np.all(gap.max() > 5)
+
+    got_w = pair_values(*[codes6_rm(QW, N, H), scales_rm(SW, N, H, 32)], N)
+    ex_w, _ = exact_values(W, N)
+    dw = got_w - ex_w
+    y_exact = ex_x @ ex_w.T
+    bound = np.abs(d) @ np.abs(ex_w).T + np.abs(ex_x) @ np.abs(dw).T + np.abs(d) @ np.abs(dw).T
+    y = host_y(Y).astype(np.float64)
+    # fp32 accumulation on top of the bound: 2e-6 of the sum of magnitudes
+    slack = 2e-6 * (np.abs(got_x) @ np.abs(got_w).T)
+    assert np.all(np.abs(y - y_exact) <= bound + slack)
+    assert np.any(np.abs(y - y_exact) > slack)  # the moves do reach Y on these rows
