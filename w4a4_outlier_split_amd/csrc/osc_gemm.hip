@@ -624,10 +624,10 @@ hipError_t pick_nocomp(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.S == 0 || a.N == 0) return hipSuccess;
-  if (a.afmt == OSC_FP6P) return pick_comp<kFp6, kFp6, 32>(a, st);  // every S on the prefill kernel
+  if (a.afmt == OSC_FP6P) return launch_gemm_mx4(a, st);  // every S on the prefill kernel
   if (a.S <= kDecodeRows) return launch_gemm_dec(a, st);
   if (a.afmt == OSC_MXFP4) {
-    if (a.G != 16) return launch_gemm_mx4(a, st);  // 16x16 blocks (osc_gemm_mx4.hip)
+    if (a.G != 16) return launch_gemm_mx4(a, st);  // osc_gemm_mx4.hip
     return pick_comp<kFp4, kFp4, 16>(a, st);
   }
   // FP8 activations: no compensation path

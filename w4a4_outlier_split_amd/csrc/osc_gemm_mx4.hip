@@ -28,25 +28,32 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int roundup(int x, int m) { return (x + m - 1) / m * m; }
-
-template <int G, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int G, int FM, int BM, int BN, int WAVES_M, int WAVES_N>
 struct Cfg4 {
+  static constexpr bool P6 = FM == kFp6;         // E3M2 pairs (G = 16 carried by 32-wide scale blocks)
   static constexpr int NW = WAVES_M * WAVES_N;  // wavefronts per workgroup
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 blocks per wavefront
   // The loads of one stage, each one LDS-DMA of 64 lanes x 16 bytes: XB blocks of 16 activation
-  // rows (64 bytes each), WB blocks of 16 weight rows, the activation scale dwords of the tile (4
-  // rows per lane), the weight scale dwords.  Load g of the stage is issued by wave g % NW; every
-  // wave issues D of them, the slots past the last load going through a resource with no records
-  // into a spare kilobyte of the stage.
+  // rows (64 bytes each), WB blocks of 16 weight rows, for E3M2 pairs XQ / WQ blocks of 32 rows of
+  // the 32-byte second region, the activation scale dwords of the tile (4 rows per lane), the
+  // weight scale dwords.  Load g of the stage is issued by wave g % NW; every wave issues D of them,
+  // the slots past the last load going through a resource with no records into a spare kilobyte.
   static constexpr int XB = BM / 16, WB = BN / 16;
-  static constexpr int NLOAD = XB + WB + 2;
+  static constexpr int XQ = P6 ? BM / 32 : 0, WQ = P6 ? BN / 32 : 0;
+  static constexpr int NLOAD = XB + WB + XQ + WQ + 2;
   static constexpr int D = (NLOAD + NW - 1) / NW;  // loads per wave per stage
-  enum { kXRows = 0, kWRows = 1, kXScale = 2, kWScale = 3, kNone = 4 };
+  enum { kXRows = 0, kWRows = 1, kXScale = 2, kWScale = 3, kNone = 4, kXQ = 5, kWQ = 6 };
   static constexpr int kind(int g) {
-    return g < XB ? kXRows : g < XB + WB ? kWRows : g == XB + WB ? kXScale : g == XB + WB + 1 ? kWScale : kNone;
+    return g < XB                ? kXRows
+           : g < XB + WB           ? kWRows
+           : g < XB + WB + XQ      ? kXQ
+           : g < XB + WB + XQ + WQ ? kWQ
+           : g == XB + WB + XQ + WQ ? kXScale
+           : g == XB + WB + XQ + WQ + 1 ? kWScale
+                                   : kNone;
   }
+  static constexpr int CP = P6 ? 96 : 64;  // bytes per row of a code panel (a stage of 128 channels)
   // the kind of slot i when it is the same for every wave, else -1
   static constexpr int slot_kind(int i) {
     const int k = kind(NW * i);
@@ -55,7 +62,9 @@ struct Cfg4 {
     return k;
   }
   static constexpr int OFF_B = BM * 64;               // weight rows
-  static constexpr int OFF_SA = (BM + BN) * 64;       // activation scale dwords (one per row)
+  static constexpr int OFF_QA = (BM + BN) * 64;       // E3M2 pairs: activation second-region rows
+  static constexpr int OFF_QB = OFF_QA + XQ * 1024;   // E3M2 pairs: weight second-region rows
+  static constexpr int OFF_SA = OFF_QB + WQ * 1024;   // activation scale dwords (one per row)
   static constexpr int OFF_SB = OFF_SA + 1024;        // weight scale dwords
   static constexpr int OFF_J = OFF_SB + 1024;         // spare kilobyte (the empty loads)
   static constexpr int STAGE = OFF_J + 1024;
@@ -68,15 +77,15 @@ struct Cfg4 {
   static_assert(NS >= 3, "the LDS ring must hold at least 3 stages");
   static_assert(D * (NS - 2) < 64, "vmcnt range");
   static_assert(BM * YS <= NS * STAGE, "the output image must fit in the LDS ring");
-  static_assert(G == 32 || G == 64, "scale bytes per stage");
+  static_assert(G == 32 || (G == 64 && !P6), "scale bytes per stage");
 };
 
-template <int G, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int G, int FM, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX, const uint8_t* __restrict__ Bc,
     const uint8_t* __restrict__ QW, const uint8_t* __restrict__ SW, const uint8_t* __restrict__ WL,
     void* __restrict__ Y, int S, int N, int H, int KC) {
-  using C = Cfg4<G, BM, BN, WAVES_M, WAVES_N>;
+  using C = Cfg4<G, FM, BM, BN, WAVES_M, WAVES_N>;
   constexpr int NS = C::NS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * C::STAGE];
   lds_u8* const smem = (lds_u8*)smem_raw;
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     const int g = C::NW * i + wave;
     const int k = C::slot_kind(i) >= 0 ? C::slot_kind(i) : C::kind(g);
     kind[i] = k;
-    const bool xs = k == C::kXRows || k == C::kXScale;
+    const bool xs = k == C::kXRows || k == C::kXScale || k == C::kXQ;
     const int r0 = xs ? m0 : n0, rmax = (xs ? S : N) - 1;
     if (k == C::kXRows || k == C::kWRows) {
       const int blk = k == C::kXRows ? g : g - C::XB;
@@ -124,6 +133,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
       voff[i] = (uint32_t)min(r0 + r, rmax) * 64u + (uint32_t)(cc * 16);
       ccol[i] = 8 * cc;
       dst[i] = (k == C::kXRows ? 0 : C::OFF_B) + blk * 1024;
+    } else if (k == C::kXQ || k == C::kWQ) {
+      // second region: 32-byte rows, two 16-byte chunks each (the layout permutes the 8-byte
+      // pieces by row, no chunk swizzle)
+      const int blk = k == C::kXQ ? g - C::XB - C::WB : g - C::XB - C::WB - C::XQ;
+      const int p = blk * 64 + lane;
+      voff[i] = (uint32_t)min(r0 + (p >> 1), rmax) * 32u + (uint32_t)((p & 1) * 16);
+      ccol[i] = 0;
+      dst[i] = (k == C::kXQ ? C::OFF_QA : C::OFF_QB) + blk * 1024;
     } else if (k == C::kXScale || k == C::kWScale) {
       voff[i] = (uint32_t)(r0 + 4 * lane) * 4u;
       dst[i] = k == C::kXScale ? C::OFF_SA : C::OFF_SB;
@@ -139,9 +156,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   // panel 0, unused), else code panel s - ncs.  Past the last stage the ring keeps issuing the same
   // loads through resources with no records: they return zeros without touching memory (into a
   // buffer no later stage reads), so every stage has the same loads in flight and the same waits.
-  const auto null_rsrc = panel_rsrc(QX, 0);
   // MC: stage s may be a compensation stage (false: s >= ncs is known)
-  auto issue = [&](auto mc_t, int s, lds_u8* __restrict__ buf) {
+  auto issue = [&](auto mc_t, int s, lds_u8* __restrict__ buf) __attribute__((always_inline)) {
     constexpr bool MC = decltype(mc_t)::value;
     const bool live = s < nst;
     const bool comp = COMP && MC && s < ncs;
@@ -149,11 +165,16 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     // integers, so that every choice stays a scalar select rather than a branch
     const int kp = live ? (comp ? s : s - ncs) : 0;
     const int sp = live && !comp ? (G == 64 ? (s - ncs) >> 1 : s - ncs) : 0;
-    const uintptr_t bx = (uintptr_t)((comp ? Bc : QX) + (long)kp * (S * 64));
-    const uintptr_t bw = (uintptr_t)((comp ? WL : QW) + (long)kp * (N * 64));
+    // compensation panels have 64-byte rows, code panels C::CP-byte rows (E3M2 pairs: the first
+    // 64 bytes of every row, then the 32-byte second region of all R rows)
+    const uintptr_t bx = (uintptr_t)(comp ? Bc + (long)kp * (S * 64) : QX + (long)kp * (S * C::CP));
+    const uintptr_t bw = (uintptr_t)(comp ? WL + (long)kp * (N * 64) : QW + (long)kp * (N * C::CP));
+    const uintptr_t bxq = (uintptr_t)(QX + (long)kp * (S * C::CP) + S * 64);
+    const uintptr_t bwq = (uintptr_t)(QW + (long)kp * (N * C::CP) + N * 64);
     const uintptr_t bxs = (uintptr_t)(SX + (long)sp * (S * 4));
     const uintptr_t bws = (uintptr_t)(SW + (long)sp * (N * 4));
     const int nx = live ? S * 64 : 0, nw = live ? N * 64 : 0;
+    const int nxq = live && !comp ? S * 32 : 0, nwq = live && !comp ? N * 32 : 0;  // nothing for compensation
     const int nxs = live ? S * 4 : 0, nws = live ? N * 4 : 0;
     // compensation columns past KC (the padding of the last panel) are loaded from outside the
     // resource, as zeros
@@ -167,10 +188,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
         b = bx, n = nx;
       } else if (sk == C::kWRows) {
         b = bw, n = nw;
+      } else if (sk == C::kXQ) {
+        b = bxq, n = nxq;
+      } else if (sk == C::kWQ) {
+        b = bwq, n = nwq;
       } else {
         const int k = kind[i];
         b = k == C::kXRows ? bx : bw;
         n = k == C::kXRows ? nx : nw;
+        if constexpr (C::P6) {
+          b = k == C::kXQ ? bxq : b;
+          n = k == C::kXQ ? nxq : n;
+          b = k == C::kWQ ? bwq : b;
+          n = k == C::kWQ ? nwq : n;
+        }
         b = k == C::kXScale ? bxs : b;
         n = k == C::kXScale ? nxs : n;
         b = k == C::kWScale ? bws : b;
@@ -202,15 +233,24 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   const int h = lane >> 5;
   const int loff0 = lrow * 64 + (swz<64>(lrow, h) << 4);
   const int loff1 = lrow * 64 + (swz<64>(lrow, 2 + h) << 4);
+  // E3M2 pairs: block 2m + h's 24-byte fragment is 16 bytes of the first region and the 8-byte
+  // piece of the second region at position (2m + h) ^ (((r >> 1) ^ (r >> 3)) & 3) of row r; the
+  // rows of a block start at multiples of 32, so the position depends on the lane only
+  const int qperm = ((lrow >> 1) ^ (lrow >> 3)) & 3;
+  const int qoff0 = lrow * 32 + 8 * (h ^ qperm);
+  const int qoff1 = lrow * 32 + 8 * ((2 + h) ^ qperm);
   struct Frag {  // one K half of a stage: TM activation and TN weight fragments
     v4i x[C::TM], w[C::TN];
+    v8i x6[C::TM], w6[C::TN];  // E3M2 pairs: the whole 24-byte fragments (dwords 6, 7 unused)
   };
   struct Scales {  // a stage's scale dwords, shifted so that byte opsel of the MFMA is the lane's
     uint32_t x[C::TM], w[C::TN];
   };
   auto lds4 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v4i*)p; };
   auto lds32 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) uint32_t*)p; };
-  auto read_half = [&](int st, int m, Frag& f) {
+  auto lds8 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v2i*)p; };
+  // cs_t: a compensation stage (E3M2 pairs: no second-region reads)
+  auto read_half = [&](int st, int m, Frag& f, auto cs_t) __attribute__((always_inline)) {
     const lds_u8* As = smem + (st % NS) * C::STAGE;
     const lds_u8* Bs = As + C::OFF_B;
     const int lo = m ? loff1 : loff0;
@@ -218,9 +258,22 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     for (int i = 0; i < C::TM; ++i) f.x[i] = lds4(As + (wm * C::WTM + 32 * i) * 64 + lo);
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) f.w[j] = lds4(Bs + (wn * C::WTN + 32 * j) * 64 + lo);
+    if constexpr (C::P6 && !decltype(cs_t)::value) {
+      const int qo = m ? qoff1 : qoff0;
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const v2i q = lds8(As + C::OFF_QA + (wm * C::WTM + 32 * i) * 32 + qo);
+        f.x6[i] = __builtin_shufflevector(f.x[i], __builtin_shufflevector(q, q, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5, -1, -1);
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const v2i q = lds8(As + C::OFF_QB + (wn * C::WTN + 32 * j) * 32 + qo);
+        f.w6[j] = __builtin_shufflevector(f.w[j], __builtin_shufflevector(q, q, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5, -1, -1);
+      }
+    }
   };
   // raw scale dwords of stage st (row l % 32 of each block)
-  auto read_scales = [&](int st, Scales& sr) {
+  auto read_scales = [&](int st, Scales& sr) __attribute__((always_inline)) {
     const lds_u8* SAs = smem + (st % NS) * C::STAGE + C::OFF_SA;
     const lds_u8* SBs = smem + (st % NS) * C::STAGE + C::OFF_SB;
 #pragma unroll
@@ -231,14 +284,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   // G = 32: the stage's four bytes are 32-blocks 0..3, lane half h supplies block 2m + h: shift by
   // 8h, then opsel 2m.  G = 64: group m of the stage for both lane halves, in the half of the dword
   // that belongs to this stage (two stages share a scale dword): shift by 16 (stage parity), opsel m.
-  auto shift_scales = [&](int st, const Scales& sr, Scales& sc) {
+  auto shift_scales = [&](int st, const Scales& sr, Scales& sc) __attribute__((always_inline)) {
     const uint32_t sh = G == 32 ? 8u * (uint32_t)h : 16u * (uint32_t)((st - ncs) & 1);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) sc.x[i] = sr.x[i] >> sh;
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) sc.w[j] = sr.w[j] >> sh;
   };
-  auto mma = [&](int m, const Frag& f, const Scales& sc, bool comp) {
+  auto mma = [&](int m, const Frag& f, const Scales& sc, bool comp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -246,6 +299,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
         if (COMP && comp)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, f.w[j]),
                                                               __builtin_bit_cast(v8bf, f.x[i]), acc[i][j], 0, 0, 0);
+        else if (C::P6 && m == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w6[j], f.x6[i], acc[i][j], kFp6, kFp6, 0,
+                                                                      sc.w[j], 0, sc.x[i]);
+        else if (C::P6)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w6[j], f.x6[i], acc[i][j], kFp6, kFp6, 2,
+                                                                      sc.w[j], 2, sc.x[i]);
         else if (G == 32 && m == 0)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), widen(f.x[i]), acc[i][j], kFp4,
                                                                       kFp4, 0, sc.w[j], 0, sc.x[i]);
@@ -272,31 +331,34 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   Frag f0, f1;
   Scales sc, sr;
   // iss(s, buf): the loads of stage s into ring buffer buf
-  auto stage = [&](auto cs_t, auto ncs_t, int st, auto&& iss) {
+  auto stage = [&](auto cs_t, auto ncs_t, int st, auto&& iss) __attribute__((always_inline)) {
     constexpr bool CS = decltype(cs_t)::value, NCS = decltype(ncs_t)::value;
     iss(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE);
-    read_half(st, 1, f1);
+    read_half(st, 1, f1, cs_t);
     mma(0, f0, sc, CS);
-    Interleave<0, NM_H, C::D, NF>::run();
+    Interleave<0, NM_H, C::D, (C::P6 && !CS ? 2 : 1) * NF>::run();
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<(NS - 2) * C::D>();
     lds_barrier();
     if constexpr (!NCS) read_scales(st + 1, sr);
-    read_half(st + 1, 0, f0);
+    read_half(st + 1, 0, f0, ncs_t);
     mma(1, f1, sc, CS);
-    Interleave<0, NM_H, 0, NCS ? NF : 2 * NF>::run();
+    Interleave<0, NM_H, 0, NCS ? NF : (C::P6 ? 3 : 2) * NF>::run();
     if constexpr (!NCS) shift_scales(st + 1, sr, sc);
     __builtin_amdgcn_sched_barrier(0);
   };
   using T = std::true_type;
   using F = std::false_type;
-  auto iss_comp = [&](int s, lds_u8* buf) { issue(T{}, s, buf); };
-  auto iss_main = [&](int s, lds_u8* buf) { issue(F{}, s, buf); };
+  auto iss_comp = [&](int s, lds_u8* buf) __attribute__((always_inline)) { issue(T{}, s, buf); };
+  auto iss_main = [&](int s, lds_u8* buf) __attribute__((always_inline)) { issue(F{}, s, buf); };
 
   wait_vm<(NS - 2) * C::D>();  // stage 0 complete for this wave
   lds_barrier();
   const bool comp0 = COMP && ncs > 0;
-  read_half(0, 0, f0);
+  if (comp0)
+    read_half(0, 0, f0, std::true_type{});
+  else
+    read_half(0, 0, f0, std::false_type{});
   if (!comp0) {
     read_scales(0, sr);
     shift_scales(0, sr, sc);
@@ -312,7 +374,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   // Main stages whose loads exist: each load slot keeps its own running panel pointer, advanced by
   // a fixed stride per stage (the scale panels of G = 64 advance every other stage), so a stage
   // costs a few scalar adds instead of recomputing every base.
-  if (st + NS - 1 < nst) {
+  // (E3M2 pairs: not on this path -- its per-slot state does not fit their register budget)
+  if (!C::P6 && st + NS - 1 < nst) {
     const int s0 = st + NS - 1;  // the first stage these iterations load (a main stage)
     const int k0 = s0 - ncs;
     uintptr_t fp[C::D];
@@ -327,9 +390,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
       uint32_t sa, sb;
       if (k == C::kXRows || k == C::kWRows) {
         const int R = k == C::kXRows ? S : N;
-        b = (uintptr_t)((k == C::kXRows ? QX : QW) + (long)k0 * (R * 64));
+        b = (uintptr_t)((k == C::kXRows ? QX : QW) + (long)k0 * (R * C::CP));
         n = R * 64;
-        sa = sb = (uint32_t)(R * 64);
+        sa = sb = (uint32_t)(R * C::CP);
+      } else if (C::P6 && (k == C::kXQ || k == C::kWQ)) {
+        const int R = k == C::kXQ ? S : N;
+        b = (uintptr_t)((k == C::kXQ ? QX : QW) + (long)k0 * (R * C::CP) + R * 64);
+        n = R * 32;
+        sa = sb = (uint32_t)(R * C::CP);
       } else if (k == C::kXScale || k == C::kWScale) {
         const int R = k == C::kXScale ? S : N;
         b = (uintptr_t)((k == C::kXScale ? SX : SW) + (long)(G == 64 ? k0 >> 1 : k0) * (R * 4));
@@ -344,7 +412,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
       fp[i] = b, fn[i] = n, fsa[i] = sa, fsb[i] = sb;
     }
     auto iss_fast = [&](auto odd_t) {
-      return [&](int, lds_u8* buf) {
+      return [&](int, lds_u8* buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::D; ++i) {
           dma16(panel_rsrc((const uint8_t*)fp[i], fn[i]), voff[i], buf + dst[i]);
@@ -364,7 +432,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   // the last NS - 2 stages before the last one: their loads run past the end (empty resources)
   for (; st + 1 < nst; ++st) stage(F{}, F{}, st, iss_main);
   // the last stage: no loads of a next stage, no barrier (the epilogue starts with one)
-  read_half(nst - 1, 1, f1);
+  read_half(nst - 1, 1, f1, std::false_type{});
   mma(0, f0, sc, false);
   mma(1, f1, sc, false);
   wait_vm<0>();  // the ring's trailing loads have landed before the LDS is reused
@@ -439,11 +507,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
       }
 }
 
-template <int G, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int G, int FM, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t run4(const GemmArgs& a, hipStream_t st) {
   const int tiles = ((a.S + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm_mx4<G, COMP, YT, BM, BN, WAVES_M, WAVES_N>), dim3(tiles), dim3(WAVES_M * WAVES_N * 64), 0,
-                     st, static_cast<const uint8_t*>(a.QX), a.SX, static_cast<const uint8_t*>(a.B),
+  hipLaunchKernelGGL((k_gemm_mx4<G, FM, COMP, YT, BM, BN, WAVES_M, WAVES_N>), dim3(tiles), dim3(WAVES_M * WAVES_N * 64),
+                     0, st, static_cast<const uint8_t*>(a.QX), a.SX, static_cast<const uint8_t*>(a.B),
                      static_cast<const uint8_t*>(a.QW), a.SW, static_cast<const uint8_t*>(a.WL), a.Y, a.S, a.N, a.H,
                      a.kc);
   return hipGetLastError();
@@ -452,29 +520,30 @@ hipError_t run4(const GemmArgs& a, hipStream_t st) {
 // Tile choice (the MI355X reading of the page's "adaptive resource scheduling", §3.3): the
 // largest tile that still gives (nearly) every one of the 256 CUs a tile, since bigger tiles move
 // fewer operand bytes per product.
-template <int G, bool COMP, int YT>
+template <int G, int FM, bool COMP, int YT>
 hipError_t pick4(const GemmArgs& a, hipStream_t st) {
   constexpr long kCover = 240;  // tiles that count as covering the 256 CUs
   auto tiles = [&](int bm, int bn) { return (long)((a.S + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  if (tiles(256, 256) >= kCover) return run4<G, COMP, YT, 256, 256, 4, 2>(a, st);
-  if (a.N % 192 == 0 && tiles(256, 192) >= kCover) return run4<G, COMP, YT, 256, 192, 4, 2>(a, st);
-  if (tiles(256, 128) >= kCover) return run4<G, COMP, YT, 256, 128, 4, 2>(a, st);
-  if (tiles(128, 128) >= kCover) return run4<G, COMP, YT, 128, 128, 4, 2>(a, st);
-  return run4<G, COMP, YT, 64, 64, 2, 2>(a, st);
+  if (tiles(256, 256) >= kCover) return run4<G, FM, COMP, YT, 256, 256, 4, 2>(a, st);
+  if (a.N % 192 == 0 && tiles(256, 192) >= kCover) return run4<G, FM, COMP, YT, 256, 192, 4, 2>(a, st);
+  if (tiles(256, 128) >= kCover) return run4<G, FM, COMP, YT, 256, 128, 4, 2>(a, st);
+  if (tiles(128, 128) >= kCover) return run4<G, FM, COMP, YT, 128, 128, 4, 2>(a, st);
+  return run4<G, FM, COMP, YT, 64, 64, 2, 2>(a, st);
 }
 
-template <int G>
+template <int G, int FM>
 hipError_t pick4_comp(const GemmArgs& a, hipStream_t st) {
   const bool comp = a.B != nullptr;
-  if (a.yt == OSC_Y_F32) return comp ? pick4<G, true, OSC_Y_F32>(a, st) : pick4<G, false, OSC_Y_F32>(a, st);
-  return comp ? pick4<G, true, OSC_Y_BF16>(a, st) : pick4<G, false, OSC_Y_BF16>(a, st);
+  if (a.yt == OSC_Y_F32) return comp ? pick4<G, FM, true, OSC_Y_F32>(a, st) : pick4<G, FM, false, OSC_Y_F32>(a, st);
+  return comp ? pick4<G, FM, true, OSC_Y_BF16>(a, st) : pick4<G, FM, false, OSC_Y_BF16>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mx4(const GemmArgs& a, hipStream_t st) {
   if (a.S == 0 || a.N == 0) return hipSuccess;
-  return a.G == 32 ? pick4_comp<32>(a, st) : pick4_comp<64>(a, st);
+  if (a.afmt == OSC_FP6P) return pick4_comp<32, kFp6>(a, st);  // E3M2 pairs: 32-wide scale blocks
+  return a.G == 32 ? pick4_comp<32, kFp4>(a, st) : pick4_comp<64, kFp4>(a, st);
 }
 
 }  // namespace osc
