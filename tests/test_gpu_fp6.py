@@ -60,6 +60,25 @@ def test_quant_fp6p_bit_exact(m, data):
         np.testing.assert_array_equal(side_rm(B, S, H, 16, m), rb)
 
 
+def test_quant_fp6p_exhaustive_bf16():
+    """Every finite bf16 pattern (subnormals, zeros of both signs, the largest magnitudes), sorted,
+    reversed and shuffled, so that pairs meet scale-code gaps from 0 to over 200; one protected
+    channel per 16-group."""
+    from synth import bits_to_f32
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = np.where(np.isfinite(bits_to_f32(bits)), bits, 0).astype(np.uint16)
+    rng = np.random.default_rng(16)
+    X = np.stack([bits, bits[::-1].copy()] + [rng.permutation(bits) for _ in range(4)]).reshape(-1, 8192)
+    S, H = X.shape
+    L = rng.integers(-1, 16, (H // 16, 1)).astype(np.int32)
+    QX, SX, B = quant_multi(dev_bits16(X), S, H, 16, L, 1, FP6P)
+    torch.cuda.synchronize()
+    rq, rs, rb = oracle.quant_act_fp6p(X, L, 1)
+    np.testing.assert_array_equal(scales_rm(SX, S, H, 32), rs)
+    np.testing.assert_array_equal(codes6_rm(QX, S, H), rq)
+    np.testing.assert_array_equal(side_rm(B, S, H, 16, 1), rb)
+
+
 def _quant_plain(Xd, S, H):
     from gpu_util import _tiled_outputs
     QX, SX, _ = _tiled_outputs(S, H, 16, FP6P, False)

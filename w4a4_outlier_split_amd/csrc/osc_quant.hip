@@ -26,6 +26,8 @@ typedef short s2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef unsigned u6 __attribute__((ext_vector_type(6)));
+typedef __bf16 bf32 __attribute__((ext_vector_type(32)));
 
 __device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us2, w); }
 __device__ __forceinline__ uint32_t as_u32(us2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -37,27 +39,22 @@ __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf
 // q >= -2 is a normal E3M2 number, below that it is a multiple of 1/16 rounded to nearest, ties to
 // the even code (only when the pair's scale codes differ by more than 5).
 __device__ __forceinline__ uint32_t e2m1_to_e3m2(uint32_t c, int t) {
+  // selects only (no early return): the compiler keeps it branch-free
   const uint32_t sign = (c & 8u) << 2;
   const int mu = c & 7;
-  if (mu == 0) return sign;
   const int p = mu == 1 ? -1 : (mu >> 1) - 1;
   const int m = mu == 1 ? 0 : (mu & 1);
   const int q = p + t;
-  if (q >= -2) return sign | (uint32_t)(((q + 3) << 2) | (m << 1));
+  const uint32_t normal = (uint32_t)(((q + 3) << 2) | (m << 1));
   const int units = q == -3 ? 2 + m : q == -4 ? (m ? 2 : 1) : q == -5 ? m : 0;  // of 1/16
-  return sign | (uint32_t)units;
+  const uint32_t mag = mu == 0 ? 0u : q >= -2 ? normal : (uint32_t)units;
+  return sign | mag;
 }
 
-// The lane's 8 E2M1 codes (one dword, channel 2i in the low nibble of byte i) -> the pair's E3M2
-// codes and its stores.  The four lanes of a quad hold one 32-element block (lanes 0-1: 16-group
-// 2b, lanes 2-3: 2b+1); lane q's 8 codes are bits [48q, 48q+48) of the block's 24-byte fragment.
-__device__ __forceinline__ void pair_store(uint32_t codes4, int sx, int r, int col0, int rows,
-                                           uint8_t* __restrict__ Q, uint8_t* __restrict__ SC) {
-  const int sx_other = __builtin_amdgcn_update_dpp(0, sx, 0x4E, 0xF, 0xF, false);  // the other 16-group
-  const int hi = sx > sx_other ? sx : sx_other;
-  const int E = hi > 2 ? hi - 2 : 0;
-  const int t = sx - E;
-  uint32_t lo = 0, hi16 = 0;  // 48 bits: lo = bits 0..31, hi16 = bits 32..47
+// 8 E2M1 codes (one dword, code i in nibble i) at shift t = s_group - E_pair <= 2 -> their E3M2
+// codes, 48 bits: code i at bits [6i, 6i+6) of lo (bits 0..31) | hi16 << 32.
+__device__ __forceinline__ void e3m2_8(uint32_t codes4, int t, uint32_t& lo, uint32_t& hi16) {
+  lo = 0, hi16 = 0;
   if (t >= -1) {
     // groups within 3 scale codes of each other: every nonzero magnitude lands on a normal E3M2
     // number, code = base(mu) + 4t with base = 8 for 0.5 and 2 mu + 8 above -- four codes per
@@ -91,6 +88,19 @@ __device__ __forceinline__ void pair_store(uint32_t codes4, int sx, int r, int c
       }
     }
   }
+}
+
+// The lane's 8 E2M1 codes (one dword, channel 2i in the low nibble of byte i) -> the pair's E3M2
+// codes and its stores.  The four lanes of a quad hold one 32-element block (lanes 0-1: 16-group
+// 2b, lanes 2-3: 2b+1); lane q's 8 codes are bits [48q, 48q+48) of the block's 24-byte fragment.
+__device__ __forceinline__ void pair_store(uint32_t codes4, int sx, int r, int col0, int rows,
+                                           uint8_t* __restrict__ Q, uint8_t* __restrict__ SC) {
+  const int sx_other = __builtin_amdgcn_update_dpp(0, sx, 0x4E, 0xF, 0xF, false);  // the other 16-group
+  const int hi = sx > sx_other ? sx : sx_other;
+  const int E = hi > 2 ? hi - 2 : 0;
+  const int t = sx - E;
+  uint32_t lo, hi16;  // 48 bits: lo = bits 0..31, hi16 = bits 32..47
+  e3m2_8(codes4, t, lo, hi16);
   // every lane of the quad learns the four 48-bit pieces
   const uint32_t lo0 = __builtin_amdgcn_update_dpp(0, lo, 0x00, 0xF, 0xF, false);
   const uint32_t lo1 = __builtin_amdgcn_update_dpp(0, lo, 0x55, 0xF, 0xF, false);
@@ -305,6 +315,142 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int row
   }
 }
 
+// E3M2 pairs with one 32-element block (the two 16-groups of a pair) per lane: both group scales,
+// the pair scale and all 32 codes are formed in the lane, so the 24-byte fragment leaves in one
+// 16-byte and one 8-byte store without cross-lane assembly.  A wavefront covers 16 rows of one
+// 128-channel panel (lane l: row l / 4, block l % 4): each row's 256 bytes of X, 1 KiB of first
+// regions and 512 bytes of second regions per store instruction, and 64 consecutive scale bytes.
+// Extraction, zeroing, the E8M0 code of each zeroed group and its scaled E2M1 conversion are
+// quant_chunk's; the re-encoding to E3M2 is done by the conversion instructions (E2M1 back to bf16
+// at the relative scale, then all 32 values to E3M2 in one instruction) instead of pair_store's
+// integer form, which the wavefront layout of the gated path keeps.
+constexpr int kPairRows = 16;
+
+template <int MODE, int M>
+__global__ __launch_bounds__(256) void k_quant_pairs(const u4* __restrict__ X, int rows, int H, TableArg tab,
+                                                     uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
+                                                     uint16_t* __restrict__ side) {
+  const int npan = H >> 7;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave -> (row block, panel), panel fastest
+  const int rb = w / npan;
+  const int p = w - rb * npan;
+  const int lane = threadIdx.x & 63;
+  const int b = lane & 3;  // block of the panel
+  const int r = rb * kPairRows + (lane >> 2);
+  if (r >= rows) return;  // no cross-lane step below: each lane stands alone
+  const int col0 = p * 128 + b * 32;
+  const u4* src = X + (long)r * (H >> 3) + (col0 >> 3);
+  uint32_t x[16], v[16];  // dword j: channels col0 + 2j (low half), 2j + 1
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u4 t = src[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * c + i] = v[4 * c + i] = t[i];
+  }
+  if (MODE != kNoTable) {
+    // entry e of group k (k = col0 / 16 + g) goes to compensation column k*m + e (+0 for -1)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int k = (col0 >> 4) + g;
+#pragma unroll
+      for (int e = 0; e < M; ++e) {
+        const int ent = tab.v[k * M + e];
+        const int d = ent >> 1;
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) word = d == j ? x[8 * g + j] : word;
+        const uint32_t val = ent < 0 ? 0u : (ent & 1) ? (word >> 16) : (word & 0xFFFFu);
+        if (MODE == kExtractZero) {
+          const uint32_t keep = (ent & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[8 * g + j] = ent >= 0 && d == j ? (v[8 * g + j] & keep) : v[8 * g + j];
+        }
+        const int col = k * M + e;
+        side[((long)(col >> 5) * rows + r) * 32 + (col & 31)] = (uint16_t)val;
+      }
+    }
+  }
+  int sx[2];
+  uint32_t codes4[4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    us2 mx = as_us2(v[8 * g] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = __builtin_elementwise_max(mx, as_us2(v[8 * g + j] & 0x7FFF7FFFu));
+    const int amax = mx.x > mx.y ? mx.x : mx.y;
+    const int E = amax >> 7;
+    sx[g] = E > 2 ? E - 2 : 0;
+    const float scale = __builtin_bit_cast(float, (uint32_t)sx[g] << 23);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint32_t out = 0;
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh]), scale, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh + 1]), scale, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh + 2]), scale, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh + 3]), scale, 3);
+      codes4[2 * g + hh] = out;
+    }
+  }
+  const int hi = sx[0] > sx[1] ? sx[0] : sx[1];
+  const int Ep = hi > 2 ? hi - 2 : 0;
+  // Each group's E2M1 values back as bf16, times 2^t with t = s_group - E_pair <= 2 (exact: at most
+  // 24 in magnitude), then one conversion of all 32 values to E3M2 at unit scale: exact where the
+  // value is an E3M2 number, else rounded to nearest, ties to the even code.  Below t = -10 every
+  // magnitude is under 1/32 and becomes a signed zero either way, so t is floored there.
+  bf32 y;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int t = sx[g] - Ep > -10 ? sx[g] - Ep : -10;
+    const float rel = __builtin_bit_cast(float, (uint32_t)(127 + t) << 23);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t c = codes4[2 * g + hh];
+      const int o = 16 * g + 8 * hh;
+      const bf2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 0);
+      const bf2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 1);
+      const bf2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 2);
+      const bf2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 3);
+      y[o + 0] = a0[0], y[o + 1] = a0[1], y[o + 2] = a1[0], y[o + 3] = a1[1];
+      y[o + 4] = a2[0], y[o + 5] = a2[1], y[o + 6] = a3[0], y[o + 7] = a3[1];
+    }
+  }
+  const u6 f = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(y, 1.0f);
+  // the 24-byte fragment (code i at bits [6i, 6i + 6)): 16 bytes to the first region, 8 to the second
+  const u4 first = {f[0], f[1], f[2], f[3]};
+  const u2 second = {f[4], f[5]};
+  const long stage = (long)p * rows * 96;
+  __builtin_nontemporal_store(first, reinterpret_cast<u4*>(Q + stage + (long)r * 64 + b * 16));
+  __builtin_nontemporal_store(
+      second, reinterpret_cast<u2*>(Q + stage + (long)rows * 64 + (long)r * 32 + 8 * (b ^ (((r >> 1) ^ (r >> 3)) & 3))));
+  SC[((long)p * rows + r) * 4 + b] = (uint8_t)Ep;
+}
+
+template <int MODE>
+hipError_t launch_pairs_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC,
+                          uint16_t* sd, unsigned grid, hipStream_t st) {
+  switch (m) {
+    case 1: hipLaunchKernelGGL((k_quant_pairs<MODE, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 2: hipLaunchKernelGGL((k_quant_pairs<MODE, 2>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    default: hipLaunchKernelGGL((k_quant_pairs<MODE, 3>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t dispatch_pairs(const void* X, int rows, int H, int m, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+                          void* side, hipStream_t st) {
+  const long waves = (long)((rows + kPairRows - 1) / kPairRows) * (H >> 7);
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const u4* x = static_cast<const u4*>(X);
+  uint8_t* q = static_cast<uint8_t*>(Q);
+  uint16_t* sd = static_cast<uint16_t*>(side);
+  static const TableArg empty = {};
+  const TableArg& t = tab ? *tab : empty;
+  if (mode == kExtractZero) return launch_pairs_m<kExtractZero>(x, rows, H, m, t, q, SC, sd, grid, st);
+  if (mode == kCopyOnly) return launch_pairs_m<kCopyOnly>(x, rows, H, m, t, q, SC, sd, grid, st);
+  hipLaunchKernelGGL((k_quant_pairs<kNoTable, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
+  return hipGetLastError();
+}
+
 template <int G, int FMT, int MODE, bool GLU>
 hipError_t launch_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC, uint16_t* sd,
                     unsigned grid, hipStream_t st) {
@@ -353,7 +499,7 @@ hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* t
   if (fmt == OSC_FP6P) {
     if constexpr (G == 16) {
       if (glu) return dispatch_glu<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
-      return dispatch_mode<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
+      return dispatch_pairs(X, rows, H, m, tab, mode, Q, SC, side, st);
     }
     return hipErrorInvalidValue;  // E3M2 pairs exist for G = 16 only
   }
