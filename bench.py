@@ -169,15 +169,22 @@ SETTLE_S = 0.3
 
 
 def settle(torch, body, seconds):
-    """Untimed repetitions of body() for at least `seconds` of wall time (chunks of 64, each
-    synchronized), so that the timed region starts with the device at its loaded clocks."""
+    """Untimed repetitions of body() for at least `seconds` of wall time, so that the timed region
+    starts with the device at its loaded clocks.  The host runs at most two chunks of 64 ahead of
+    the device (an event per chunk) and does not drain the queue at the end: the warm-up steps
+    enqueued next follow without the device going idle in between."""
     t0 = time.perf_counter()
     n = 0
+    pending = []
     while time.perf_counter() - t0 < seconds:
         for _ in range(64):
             body(n)
             n += 1
-        torch.cuda.synchronize()
+        e = torch.cuda.Event()
+        e.record()
+        pending.append(e)
+        if len(pending) > 2:
+            pending.pop(0).synchronize()
     return n
 
 
@@ -196,13 +203,15 @@ def time_layer(torch, osc, sets, steps, warmup, stream):
         quant(l)
         gemm(l)
 
+    # host work that could leave the device idle (collection, event creation) comes before the
+    # untimed steps, which then run without a gap up to the synchronization that opens the timed region
+    ev = TimingEvents(2 * steps + 3)
+    gc.collect()
+    gc.disable()  # no collector pause inside the timed region
     with torch.cuda.stream(stream):
         settle(torch, one, SETTLE_S)
         for i in range(warmup):
             one(i)
-        ev = TimingEvents(2 * steps + 3)
-        gc.collect()
-        gc.disable()  # no collector pause inside the timed region
         # pass 1: the step time, steps back to back
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -530,15 +539,15 @@ def run_block(torch, osc, dev, stream, steps, warmup, S=4096):
         Ym = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
         calls = [lambda: q.forward(Xq, S, aq, Yq, stream=stream), lambda: o.forward(Xo, S, ao, Yo, stream=stream),
                  lambda: mlp.forward(Xu, S, bufs, Ym, stream=stream)]
+        ev = TimingEvents(2 + 4 * steps)
+        sh = stream.cuda_stream
+        gc.collect()
+        gc.disable()
         with torch.cuda.stream(stream):
             settle(torch, lambda _: [c() for c in calls], SETTLE_S)
             for _ in range(warmup):
                 for c in calls:
                     c()
-            ev = TimingEvents(2 + 4 * steps)
-            sh = stream.cuda_stream
-            gc.collect()
-            gc.disable()
             torch.cuda.synchronize()
             ev.record(0, sh)
             for _ in range(steps):
