@@ -47,6 +47,30 @@ def test_quant_multi_bit_exact(G, m):
     np.testing.assert_array_equal(side_rm(B, S, H, G, m), rb)
 
 
+@pytest.mark.parametrize("G,m", [(16, 2), (16, 3), (32, 2), (64, 3)])
+def test_quant_multi_entries_sharing_a_dword(G, m):
+    """Entries on the two channels of one 32-bit word of X (2j and 2j+1, listed in either order),
+    and for G = 64 entries in both halves of the group: each listed slot is zeroed and copied."""
+    S, H = 40, 1024
+    X = synth.random_bf16((S, H), seed=G + 10 * m, scale=3.0)
+    rng = np.random.default_rng(G + m)
+    K = H // G
+    L = np.full((K, m), -1, np.int32)
+    for k in range(K):
+        j = 2 * int(rng.integers(0, G // 2))
+        pair = [j, j + 1] if k % 2 else [j + 1, j]
+        rest = [c for c in rng.permutation(G) if c not in pair]
+        if G == 64:  # the third entry in the other half
+            rest = [c for c in rest if (c >= 32) != (j >= 32)]
+        L[k] = (pair + rest)[:m]
+    QX, SX, B = quant_multi(dev_bits16(X), S, H, G, L, m)
+    torch.cuda.synchronize()
+    rq, rs, rb = oracle.quant_act_multi(X, G, L, m)
+    np.testing.assert_array_equal(codes_rm(QX, S, H, osc.OSC_MXFP4), rq)
+    np.testing.assert_array_equal(scales_rm(SX, S, H, G), rs)
+    np.testing.assert_array_equal(side_rm(B, S, H, G, m), rb)
+
+
 def test_quant_and_pack_two_outlier_workload():
     w = two()
     QX, SX, B = quant_multi(dev_bits16(w.X), w.S, w.H, w.G, w.L, 2)

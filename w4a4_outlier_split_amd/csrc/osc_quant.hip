@@ -315,29 +315,49 @@ __global__ __launch_bounds__(256) void k_quant(const u4* __restrict__ X, int row
   }
 }
 
-// E3M2 pairs with one 32-element block (the two 16-groups of a pair) per lane: both group scales,
-// the pair scale and all 32 codes are formed in the lane, so the 24-byte fragment leaves in one
-// 16-byte and one 8-byte store without cross-lane assembly.  A wavefront covers 16 rows of one
-// 128-channel panel (lane l: row l / 4, block l % 4): each row's 256 bytes of X, 1 KiB of first
-// regions and 512 bytes of second regions per store instruction, and 64 consecutive scale bytes.
-// Extraction, zeroing, the E8M0 code of each zeroed group and its scaled E2M1 conversion are
-// quant_chunk's; the re-encoding to E3M2 is done by the conversion instructions (E2M1 back to bf16
-// at the relative scale, then all 32 values to E3M2 in one instruction) instead of pair_store's
-// integer form, which the wavefront layout of the gated path keeps.
-constexpr int kPairRows = 16;
+// One 32-channel block of one row per lane, for E2M1 codes at G = 16 / 32 / 64 and for E3M2 pairs.
+// A wavefront covers 16 rows of one 128-channel panel (lane l: row l / 4, block b = l % 4), loading
+// each row's 256 bytes as four 16-byte pieces per lane; every code store instruction writes 1 KiB
+// of the panel (pairs: 1 KiB of first regions and 512 bytes of second regions), and the scale bytes
+// of the 16 rows are contiguous.  The block holds two 16-groups (G = 16 and the pairs), one group
+// (G = 32), or half of one (G = 64: the halves sit in neighbouring lanes of the same row and meet
+// in one DPP lane swap for the amax).  The arithmetic is quant_chunk's: extraction, zeroing, the
+// E8M0 code of the zeroed group, the scaled E2M1 conversion.  Pairs then re-encode to E3M2 with the
+// conversion instructions (E2M1 back to bf16 at the relative scale, all 32 values to E3M2 in one
+// instruction) instead of pair_store's integer form, which the gated path (quant_chunk's lanes)
+// keeps.
+constexpr int kBlkRows = 16;
 
-template <int MODE, int M>
-__global__ __launch_bounds__(256) void k_quant_pairs(const u4* __restrict__ X, int rows, int H, TableArg tab,
-                                                     uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
-                                                     uint16_t* __restrict__ side) {
+// dword d (lane-varying, 0 <= d < N) of the N words w[0..N), by a binary tree of selects on d's bits
+template <int N>
+__device__ __forceinline__ uint32_t pick(const uint32_t* w, int d) {
+  uint32_t t[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) t[j] = w[j];
+#pragma unroll
+  for (int n = N, bit = 1; n > 1; n >>= 1, bit <<= 1) {
+    const bool hi = (d & bit) != 0;
+#pragma unroll
+    for (int j = 0; j < n / 2; ++j) t[j] = hi ? t[2 * j + 1] : t[2 * j];
+  }
+  return t[0];
+}
+
+template <int G, int FMT, int MODE, int M>
+__global__ __launch_bounds__(256) void k_quant_blk(const u4* __restrict__ X, int rows, int H, TableArg tab,
+                                                   uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
+                                                   uint16_t* __restrict__ side) {
+  static_assert(FMT == OSC_MXFP4 || (FMT == OSC_FP6P && G == 16), "E2M1 codes, or E3M2 pairs of 16-groups");
+  constexpr int NG = G == 16 ? 2 : 1;  // groups (G = 64: group halves) in the block
+  constexpr int GW = 16 / NG;           // dwords of each
   const int npan = H >> 7;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave -> (row block, panel), panel fastest
   const int rb = w / npan;
   const int p = w - rb * npan;
   const int lane = threadIdx.x & 63;
   const int b = lane & 3;  // block of the panel
-  const int r = rb * kPairRows + (lane >> 2);
-  if (r >= rows) return;  // no cross-lane step below: each lane stands alone
+  const int r = rb * kBlkRows + (lane >> 2);
+  if (r >= rows) return;  // a row's four lanes leave together: the G = 64 swap stays inside a row
   const int col0 = p * 128 + b * 32;
   const u4* src = X + (long)r * (H >> 3) + (col0 >> 3);
   uint32_t x[16], v[16];  // dword j: channels col0 + 2j (low half), 2j + 1
@@ -348,106 +368,129 @@ __global__ __launch_bounds__(256) void k_quant_pairs(const u4* __restrict__ X, i
     for (int i = 0; i < 4; ++i) x[4 * c + i] = v[4 * c + i] = t[i];
   }
   if (MODE != kNoTable) {
-    // entry e of group k (k = col0 / 16 + g) goes to compensation column k*m + e (+0 for -1)
+    // entry e of group k goes to compensation column k*m + e (+0 for -1), written by the lane that
+    // holds the channel (G = 64, entry -1: the lane of the group's first half)
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int k = (col0 >> 4) + g;
+    for (int g = 0; g < NG; ++g) {
+      const int k = G == 64 ? col0 >> 6 : G == 32 ? col0 >> 5 : (col0 >> 4) + g;
+      const int base = G == 64 ? (b & 1) * 32 : 0;  // the group's channel at this lane's dword 0
 #pragma unroll
       for (int e = 0; e < M; ++e) {
         const int ent = tab.v[k * M + e];
-        const int d = ent >> 1;
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) word = d == j ? x[8 * g + j] : word;
-        const uint32_t val = ent < 0 ? 0u : (ent & 1) ? (word >> 16) : (word & 0xFFFFu);
+        const int loc = ent - base;
+        const bool own = ent >= 0 && loc < 2 * GW && (G != 64 || loc >= 0);
+        const int d = loc >> 1;
+        const uint32_t word = pick<GW>(x + GW * g, d & (GW - 1));
+        const uint32_t val = own ? ((ent & 1) ? (word >> 16) : (word & 0xFFFFu)) : 0u;
         if (MODE == kExtractZero) {
+          // masked in the running copy: two entries may share a dword
           const uint32_t keep = (ent & 1) ? 0x0000FFFFu : 0xFFFF0000u;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[8 * g + j] = ent >= 0 && d == j ? (v[8 * g + j] & keep) : v[8 * g + j];
+          for (int j = 0; j < GW; ++j) v[GW * g + j] = own && d == j ? (v[GW * g + j] & keep) : v[GW * g + j];
         }
         const int col = k * M + e;
-        side[((long)(col >> 5) * rows + r) * 32 + (col & 31)] = (uint16_t)val;
+        if (G != 64 || own || (ent < 0 && (b & 1) == 0))
+          side[((long)(col >> 5) * rows + r) * 32 + (col & 31)] = (uint16_t)val;
       }
     }
   }
-  int sx[2];
+  int sx[NG];
   uint32_t codes4[4];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    us2 mx = as_us2(v[8 * g] & 0x7FFF7FFFu);
+  for (int g = 0; g < NG; ++g) {
+    us2 mx = as_us2(v[GW * g] & 0x7FFF7FFFu);
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = __builtin_elementwise_max(mx, as_us2(v[8 * g + j] & 0x7FFF7FFFu));
-    const int amax = mx.x > mx.y ? mx.x : mx.y;
+    for (int j = 1; j < GW; ++j) mx = __builtin_elementwise_max(mx, as_us2(v[GW * g + j] & 0x7FFF7FFFu));
+    int amax = mx.x > mx.y ? mx.x : mx.y;
+    if constexpr (G == 64) amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0xB1, 0xF, 0xF, false));
     const int E = amax >> 7;
     sx[g] = E > 2 ? E - 2 : 0;
-    const float scale = __builtin_bit_cast(float, (uint32_t)sx[g] << 23);
+    const float scale = __builtin_bit_cast(float, (uint32_t)sx[g] << 23);  // only the exponent field is used
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < GW / 4; ++hh) {
+      const uint32_t* s4 = v + GW * g + 4 * hh;
       uint32_t out = 0;
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh]), scale, 0);
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh + 1]), scale, 1);
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh + 2]), scale, 2);
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(v[8 * g + 4 * hh + 3]), scale, 3);
-      codes4[2 * g + hh] = out;
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(s4[0]), scale, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(s4[1]), scale, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(s4[2]), scale, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(s4[3]), scale, 3);
+      codes4[(GW / 4) * g + hh] = out;
     }
   }
-  const int hi = sx[0] > sx[1] ? sx[0] : sx[1];
-  const int Ep = hi > 2 ? hi - 2 : 0;
-  // Each group's E2M1 values back as bf16, times 2^t with t = s_group - E_pair <= 2 (exact: at most
-  // 24 in magnitude), then one conversion of all 32 values to E3M2 at unit scale: exact where the
-  // value is an E3M2 number, else rounded to nearest, ties to the even code.  Below t = -10 every
-  // magnitude is under 1/32 and becomes a signed zero either way, so t is floored there.
-  bf32 y;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int t = sx[g] - Ep > -10 ? sx[g] - Ep : -10;
-    const float rel = __builtin_bit_cast(float, (uint32_t)(127 + t) << 23);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const uint32_t c = codes4[2 * g + hh];
-      const int o = 16 * g + 8 * hh;
-      const bf2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 0);
-      const bf2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 1);
-      const bf2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 2);
-      const bf2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 3);
-      y[o + 0] = a0[0], y[o + 1] = a0[1], y[o + 2] = a1[0], y[o + 3] = a1[1];
-      y[o + 4] = a2[0], y[o + 5] = a2[1], y[o + 6] = a3[0], y[o + 7] = a3[1];
+  if constexpr (FMT == OSC_MXFP4) {
+    // codes: the block's 16 bytes of the row's 64 in the panel; scales at G = 16 in panels of 8
+    // groups (this block's two adjacent), else of 4
+    const u4 c = {codes4[0], codes4[1], codes4[2], codes4[3]};
+    __builtin_nontemporal_store(c, reinterpret_cast<u4*>(Q + ((long)p * rows + r) * 64 + b * 16));
+    if constexpr (G == 16) {
+      *reinterpret_cast<uint16_t*>(SC + ((long)p * rows + r) * 8 + 2 * b) = (uint16_t)(sx[0] | (sx[1] << 8));
+    } else if constexpr (G == 32) {
+      SC[((long)p * rows + r) * 4 + b] = (uint8_t)sx[0];
+    } else {
+      const int k = col0 >> 6;
+      if ((b & 1) == 0) SC[((long)(k >> 2) * rows + r) * 4 + (k & 3)] = (uint8_t)sx[0];
     }
+  } else {
+    const int hi = sx[0] > sx[1] ? sx[0] : sx[1];
+    const int Ep = hi > 2 ? hi - 2 : 0;
+    // Each group's E2M1 values back as bf16, times 2^t with t = s_group - E_pair <= 2 (exact: at
+    // most 24 in magnitude), then one conversion of all 32 values to E3M2 at unit scale: exact
+    // where the value is an E3M2 number, else rounded to nearest, ties to the even code.  Below
+    // t = -10 every magnitude is under 1/32 and becomes a signed zero either way, so t is floored.
+    bf32 y;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int t = sx[g] - Ep > -10 ? sx[g] - Ep : -10;
+      const float rel = __builtin_bit_cast(float, (uint32_t)(127 + t) << 23);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t c = codes4[2 * g + hh];
+        const int o = 16 * g + 8 * hh;
+        const bf2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 0);
+        const bf2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 1);
+        const bf2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 2);
+        const bf2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, rel, 3);
+        y[o + 0] = a0[0], y[o + 1] = a0[1], y[o + 2] = a1[0], y[o + 3] = a1[1];
+        y[o + 4] = a2[0], y[o + 5] = a2[1], y[o + 6] = a3[0], y[o + 7] = a3[1];
+      }
+    }
+    const u6 f = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(y, 1.0f);
+    // the 24-byte fragment (code i at bits [6i, 6i + 6)): 16 bytes to the first region, 8 to the
+    // second, whose 8-byte pieces sit at position b ^ (((r >> 1) ^ (r >> 3)) & 3) in the row
+    const u4 first = {f[0], f[1], f[2], f[3]};
+    const u2 second = {f[4], f[5]};
+    const long stage = (long)p * rows * 96;
+    __builtin_nontemporal_store(first, reinterpret_cast<u4*>(Q + stage + (long)r * 64 + b * 16));
+    __builtin_nontemporal_store(
+        second, reinterpret_cast<u2*>(Q + stage + (long)rows * 64 + (long)r * 32 + 8 * (b ^ (((r >> 1) ^ (r >> 3)) & 3))));
+    SC[((long)p * rows + r) * 4 + b] = (uint8_t)Ep;
   }
-  const u6 f = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(y, 1.0f);
-  // the 24-byte fragment (code i at bits [6i, 6i + 6)): 16 bytes to the first region, 8 to the second
-  const u4 first = {f[0], f[1], f[2], f[3]};
-  const u2 second = {f[4], f[5]};
-  const long stage = (long)p * rows * 96;
-  __builtin_nontemporal_store(first, reinterpret_cast<u4*>(Q + stage + (long)r * 64 + b * 16));
-  __builtin_nontemporal_store(
-      second, reinterpret_cast<u2*>(Q + stage + (long)rows * 64 + (long)r * 32 + 8 * (b ^ (((r >> 1) ^ (r >> 3)) & 3))));
-  SC[((long)p * rows + r) * 4 + b] = (uint8_t)Ep;
 }
 
-template <int MODE>
-hipError_t launch_pairs_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC,
-                          uint16_t* sd, unsigned grid, hipStream_t st) {
+template <int G, int FMT, int MODE>
+hipError_t launch_blk_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC,
+                        uint16_t* sd, unsigned grid, hipStream_t st) {
   switch (m) {
-    case 1: hipLaunchKernelGGL((k_quant_pairs<MODE, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
-    case 2: hipLaunchKernelGGL((k_quant_pairs<MODE, 2>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
-    default: hipLaunchKernelGGL((k_quant_pairs<MODE, 3>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 1: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 2: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 2>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    default: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 3>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
   }
   return hipGetLastError();
 }
 
-hipError_t dispatch_pairs(const void* X, int rows, int H, int m, const TableArg* tab, int mode, void* Q, uint8_t* SC,
-                          void* side, hipStream_t st) {
-  const long waves = (long)((rows + kPairRows - 1) / kPairRows) * (H >> 7);
+template <int G, int FMT>
+hipError_t dispatch_blk(const void* X, int rows, int H, int m, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+                        void* side, hipStream_t st) {
+  const long waves = (long)((rows + kBlkRows - 1) / kBlkRows) * (H >> 7);
   const unsigned grid = (unsigned)((waves + 3) / 4);
   const u4* x = static_cast<const u4*>(X);
   uint8_t* q = static_cast<uint8_t*>(Q);
   uint16_t* sd = static_cast<uint16_t*>(side);
   static const TableArg empty = {};
   const TableArg& t = tab ? *tab : empty;
-  if (mode == kExtractZero) return launch_pairs_m<kExtractZero>(x, rows, H, m, t, q, SC, sd, grid, st);
-  if (mode == kCopyOnly) return launch_pairs_m<kCopyOnly>(x, rows, H, m, t, q, SC, sd, grid, st);
-  hipLaunchKernelGGL((k_quant_pairs<kNoTable, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
+  if (mode == kExtractZero) return launch_blk_m<G, FMT, kExtractZero>(x, rows, H, m, t, q, SC, sd, grid, st);
+  if (mode == kCopyOnly) return launch_blk_m<G, FMT, kCopyOnly>(x, rows, H, m, t, q, SC, sd, grid, st);
+  hipLaunchKernelGGL((k_quant_blk<G, FMT, kNoTable, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   return hipGetLastError();
 }
 
@@ -499,7 +542,7 @@ hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* t
   if (fmt == OSC_FP6P) {
     if constexpr (G == 16) {
       if (glu) return dispatch_glu<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
-      return dispatch_pairs(X, rows, H, m, tab, mode, Q, SC, side, st);
+      return dispatch_blk<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
     }
     return hipErrorInvalidValue;  // E3M2 pairs exist for G = 16 only
   }
@@ -507,7 +550,7 @@ hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* t
     if (fmt == OSC_MXFP4) return dispatch_glu<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
     return dispatch_glu<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
   }
-  if (fmt == OSC_MXFP4) return dispatch_mode<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
+  if (fmt == OSC_MXFP4) return dispatch_blk<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
   return dispatch_mode<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
 }
 
