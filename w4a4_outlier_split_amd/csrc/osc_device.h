@@ -73,6 +73,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const uint8_t* base
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_u8* __restrict__ l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, off, 0, 0, 0);
 }
+// the same with a scalar offset (inside the range check as well)
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff, lds_u8* __restrict__ l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, off, soff, 0, 0);
+}
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_u8* __restrict__ l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, off, 0, 0, 0);
 }

@@ -28,6 +28,18 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// fn(std::integral_constant<int, I>{}) for I = B .. E - 1, in order
+template <int B, int E>
+struct RingFor {
+  template <class Fn>
+  __device__ __forceinline__ static void run(Fn&& fn) {
+    if constexpr (B < E) {
+      fn(std::integral_constant<int, B>{});
+      RingFor<B + 1, E>::run(fn);
+    }
+  }
+};
+
 template <int G, int FM, int BM, int BN, int WAVES_M, int WAVES_N>
 struct Cfg4 {
   static constexpr bool P6 = FM == kFp6;         // E3M2 pairs (G = 16 carried by 32-wide scale blocks)
@@ -250,8 +262,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   auto lds32 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) uint32_t*)p; };
   auto lds8 = [&](const lds_u8* p) { return *(const __attribute__((address_space(3))) v2i*)p; };
   // cs_t: a compensation stage (E3M2 pairs: no second-region reads)
-  auto read_half = [&](int st, int m, Frag& f, auto cs_t) __attribute__((always_inline)) {
-    const lds_u8* As = smem + (st % NS) * C::STAGE;
+  // q: the stage's ring buffer (a constant where the caller's loop is unrolled over the ring)
+  auto read_half = [&](int q, int m, Frag& f, auto cs_t) __attribute__((always_inline)) {
+    const lds_u8* As = smem + q * C::STAGE;
     const lds_u8* Bs = As + C::OFF_B;
     const int lo = m ? loff1 : loff0;
 #pragma unroll
@@ -273,9 +286,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     }
   };
   // raw scale dwords of stage st (row l % 32 of each block)
-  auto read_scales = [&](int st, Scales& sr) __attribute__((always_inline)) {
-    const lds_u8* SAs = smem + (st % NS) * C::STAGE + C::OFF_SA;
-    const lds_u8* SBs = smem + (st % NS) * C::STAGE + C::OFF_SB;
+  auto read_scales = [&](int q, Scales& sr) __attribute__((always_inline)) {
+    const lds_u8* SAs = smem + q * C::STAGE + C::OFF_SA;
+    const lds_u8* SBs = smem + q * C::STAGE + C::OFF_SB;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) sr.x[i] = lds32(SAs + (wm * C::WTM + 32 * i + lrow) * 4);
 #pragma unroll
@@ -331,17 +344,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   Frag f0, f1;
   Scales sc, sr;
   // iss(s, buf): the loads of stage s into ring buffer buf
-  auto stage = [&](auto cs_t, auto ncs_t, int st, auto&& iss) __attribute__((always_inline)) {
+  // q = st % NS, the ring buffer of stage st
+  auto stage = [&](auto cs_t, auto ncs_t, int st, int q, auto&& iss) __attribute__((always_inline)) {
     constexpr bool CS = decltype(cs_t)::value, NCS = decltype(ncs_t)::value;
-    iss(st + NS - 1, smem + ((st + NS - 1) % NS) * C::STAGE);
-    read_half(st, 1, f1, cs_t);
+    constexpr bool POW2 = (NS & (NS - 1)) == 0;
+    const int q1 = POW2 ? (q + 1) & (NS - 1) : (q + 1 == NS ? 0 : q + 1);  // stage st + 1
+    const int qn = POW2 ? (q + NS - 1) & (NS - 1) : (q == 0 ? NS - 1 : q - 1);  // stage st + NS - 1
+    iss(st + NS - 1, smem + qn * C::STAGE);
+    read_half(q, 1, f1, cs_t);
     mma(0, f0, sc, CS);
     Interleave<0, NM_H, C::D, (C::P6 && !CS ? 2 : 1) * NF>::run();
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<(NS - 2) * C::D>();
     lds_barrier();
-    if constexpr (!NCS) read_scales(st + 1, sr);
-    read_half(st + 1, 0, f0, ncs_t);
+    if constexpr (!NCS) read_scales(q1, sr);
+    read_half(q1, 0, f0, ncs_t);
     mma(1, f1, sc, CS);
     Interleave<0, NM_H, 0, NCS ? NF : (C::P6 ? 3 : 2) * NF>::run();
     if constexpr (!NCS) shift_scales(st + 1, sr, sc);
@@ -365,16 +382,16 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   }
   int st = 0;
   if constexpr (COMP) {
-    for (; st + 1 < ncs; ++st) stage(T{}, T{}, st, iss_comp);
+    for (; st + 1 < ncs; ++st) stage(T{}, T{}, st, st % NS, iss_comp);
     if (st < ncs) {  // the last compensation stage hands over to the first main stage
-      stage(T{}, F{}, st, iss_comp);
+      stage(T{}, F{}, st, st % NS, iss_comp);
       ++st;
     }
   }
   // Main stages whose loads exist: each load slot keeps its own running panel pointer, advanced by
   // a fixed stride per stage (the scale panels of G = 64 advance every other stage), so a stage
   // costs a few scalar adds instead of recomputing every base.
-  // (E3M2 pairs: not on this path -- its per-slot state does not fit their register budget)
+  // (E3M2 pairs take the next loop: this one's per-slot state does not fit their register budget)
   if (!C::P6 && st + NS - 1 < nst) {
     const int s0 = st + NS - 1;  // the first stage these iterations load (a main stage)
     const int k0 = s0 - ncs;
@@ -421,18 +438,72 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
       };
     };
     for (; st + NS < nst; st += 2) {
-      stage(F{}, F{}, st, iss_fast(F{}));
-      stage(F{}, F{}, st + 1, iss_fast(T{}));
+      stage(F{}, F{}, st, st % NS, iss_fast(F{}));
+      stage(F{}, F{}, st + 1, (st + 1) % NS, iss_fast(T{}));
     }
     if (st + NS - 1 < nst) {
-      stage(F{}, F{}, st, iss_fast(F{}));
+      stage(F{}, F{}, st, st % NS, iss_fast(F{}));
       ++st;
     }
   }
+  // E3M2 pairs: each operand region is read through one descriptor over all its panels, fixed for
+  // the loop, at a scalar offset that advances one panel per stage (the range check includes it),
+  // and the loop is unrolled over the NS ring buffers so that a stage's LDS addresses are constants.
+  if constexpr (C::P6) {
+    if (st + NS - 1 < nst) {
+      const uint32_t k0 = (uint32_t)(st + NS - 1 - ncs);  // the code panel of the first stage loaded here
+      const long npan = H / 128;
+      const uint32_t dX = (uint32_t)(S * C::CP), dW = (uint32_t)(N * C::CP);
+      const auto rX = panel_rsrc(QX, npan * dX), rW = panel_rsrc(QW, npan * dW);
+      const auto rXQ = panel_rsrc(QX + S * 64, npan * dX - S * 64), rWQ = panel_rsrc(QW + N * 64, npan * dW - N * 64);
+      uint32_t oX = k0 * dX, oW = k0 * dW;
+      // the other slots (scale dwords, nothing, or a kind that differs between waves): their own state
+      constexpr auto rows = [](int k) { return k == C::kXRows || k == C::kWRows || k == C::kXQ || k == C::kWQ; };
+      __amdgpu_buffer_rsrc_t rR[C::D];
+      uint32_t oR[C::D], dR[C::D];
+#pragma unroll
+      for (int i = 0; i < C::D; ++i) {
+        if (rows(C::slot_kind(i))) continue;
+        const int k = kind[i];
+        const bool xs = k == C::kXRows || k == C::kXQ || k == C::kXScale;
+        const bool sc = k == C::kXScale || k == C::kWScale;
+        const uint32_t d = k == C::kNone ? 0u : sc ? (uint32_t)((xs ? S : N) * 4) : xs ? dX : dW;
+        const uint8_t* b = sc ? (xs ? SX : SW) : xs ? QX : QW;
+        const long off = k == C::kXQ ? S * 64 : k == C::kWQ ? N * 64 : 0;
+        rR[i] = panel_rsrc(b + off, k == C::kNone ? 0 : npan * d - off);
+        oR[i] = k0 * d, dR[i] = d;
+      }
+      auto iss6 = [&](int, lds_u8* buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < C::D; ++i) {
+          const int sk = C::slot_kind(i);
+          if (sk == C::kXRows)
+            dma16s(rX, voff[i], oX, buf + dst[i]);
+          else if (sk == C::kWRows)
+            dma16s(rW, voff[i], oW, buf + dst[i]);
+          else if (sk == C::kXQ)
+            dma16s(rXQ, voff[i], oX, buf + dst[i]);
+          else if (sk == C::kWQ)
+            dma16s(rWQ, voff[i], oW, buf + dst[i]);
+          else {
+            dma16s(rR[i], voff[i], oR[i], buf + dst[i]);
+            oR[i] += dR[i];
+          }
+        }
+        oX += dX, oW += dW;
+      };
+      for (; st % NS != 0 && st + NS - 1 < nst; ++st) stage(F{}, F{}, st, st % NS, iss6);
+      for (; st + 2 * NS - 2 < nst; st += NS)
+        RingFor<0, NS>::run([&](auto q_t) __attribute__((always_inline)) {
+          stage(F{}, F{}, st + decltype(q_t)::value, decltype(q_t)::value, iss6);
+        });
+      for (; st + NS - 1 < nst; ++st) stage(F{}, F{}, st, st % NS, iss6);
+    }
+  }
   // the last NS - 2 stages before the last one: their loads run past the end (empty resources)
-  for (; st + 1 < nst; ++st) stage(F{}, F{}, st, iss_main);
+  for (; st + 1 < nst; ++st) stage(F{}, F{}, st, st % NS, iss_main);
   // the last stage: no loads of a next stage, no barrier (the epilogue starts with one)
-  read_half(nst - 1, 1, f1, std::false_type{});
+  read_half((nst - 1) % NS, 1, f1, std::false_type{});
   mma(0, f0, sc, false);
   mma(1, f1, sc, false);
   wait_vm<0>();  // the ring's trailing loads have landed before the LDS is reused
