@@ -30,7 +30,6 @@
 // Operand fragments of the scaled MFMA (lane l: row l%32 of its operand, half h = l/32):
 //   E2M1: K [32h, 32h+32) of the 64-deep slice, 16 bytes, element 2i in the low nibble of byte i;
 //   E4M3: K [16h, 16h+16) in bytes 0..15 and [32+16h, 48+16h) in bytes 16..31;
-//   E3M2 (the G = 16 pairs): K [32h, 32h+32), 24 bytes, element i at bits [6i, 6i+6);
 //   the scale of 32-block b of row r comes from lane r + 32*b, opsel picks its byte.
 // G=64: both 32-blocks of a group use the same byte.  G=16: each 32-element hardware block holds
 // one 16-group and 16 zero codes (inserted in registers), so every MFMA covers 32 real elements.
@@ -49,7 +48,7 @@ struct Cfg {
   static constexpr int TM = WTM / 32;
   static constexpr int TN = WTN / 32;
   static constexpr int BK = 128;  // K elements per main stage
-  static constexpr int RBA = FA == kFp8 ? 128 : 64;  // E3M2: the first 64 of a row-stage's 96 bytes
+  static constexpr int RBA = FA == kFp8 ? 128 : 64;
   static constexpr int RBB = FB == kFp8 ? 128 : 64;
   static constexpr int RPI_A = 1024 / RBA;  // rows per DMA wave-instruction
   static constexpr int RPI_B = 1024 / RBB;
@@ -69,27 +68,16 @@ struct Cfg {
   static constexpr int SCA = SROWS_A / SRPI / NCW; // scale DMA instructions per X-side wave
   static constexpr int SCB = SROWS_B / SRPI / NCW;
   static constexpr int SCMAX = SCA > SCB ? SCA : SCB;
-  // E3M2 pairs: the last 32 bytes of each row-stage travel as a second region, 32 rows per
-  // wave-instruction
-  static constexpr bool P6 = FA == kFp6;
-  static constexpr int QROWS_A = P6 ? (BM + NCW * 32 - 1) / (NCW * 32) * (NCW * 32) : 0;
-  static constexpr int QROWS_B = P6 ? (BN + NCW * 32 - 1) / (NCW * 32) * (NCW * 32) : 0;
-  static constexpr int NQA = QROWS_A / 32 / NCW;
-  static constexpr int NQB = QROWS_B / 32 / NCW;
-  static constexpr int NQMAX = NQA > NQB ? NQA : NQB;
-  static constexpr int DA = NIA + SCA + NQA;       // DMA instructions per wave per stage
-  static constexpr int DB = NIB + SCB + NQB;
+  static constexpr int DA = NIA + SCA;             // DMA instructions per wave per stage
+  static constexpr int DB = NIB + SCB;
   static constexpr int OFF_B = AROWS * RBA;
   static constexpr int OFF_SA = OFF_B + BROWS * RBB;
   static constexpr int OFF_SB = OFF_SA + SROWS_A * SBL;
-  static constexpr int OFF_QA = OFF_SB + SROWS_B * SBL;
-  static constexpr int OFF_QB = OFF_QA + QROWS_A * 32;
-  static constexpr int STAGE = OFF_QB + QROWS_B * 32;
+  static constexpr int STAGE = OFF_SB + SROWS_B * SBL;
   static constexpr int NMF = (G == 16) ? 4 : 2;    // scaled MFMAs per stage per block
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert((FA == kFp6) == (FB == kFp6), "E3M2 pairs on both operands");
-  static_assert(!COMP || ((FA == kFp4 || FA == kFp6) && FB == FA),
-                "compensation stages reuse the 64-byte row geometry of the E2M1 / E3M2 code regions");
+  static_assert(FA != kFp6 && FB != kFp6, "E3M2 pairs run on the other prefill kernel");
+  static_assert(!COMP || (FA == kFp4 && FB == FA), "compensation stages reuse the 64-byte row geometry of E2M1 codes");
 };
 
 template <int FA, int FB, int G, int BM, int BN, int WAVES_M, int WAVES_N>
@@ -109,7 +97,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * C::STAGE];
   lds_u8* const smem = (lds_u8*)smem_raw;
 
-  const int K = H / G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,8 +145,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   // registers), plus the lane's fixed 32-bit offset inside the panel (rows < 2^24 of at most 128
   // bytes): no per-stage vector address arithmetic.  With compensation both sides have 64-byte rows, so the code and
   // the B / W_L panels share the offsets.
-  const long code_panel = (long)R * (C::P6 ? 96 : rb_l);  // stage stride of the codes
-  const long code_bytes = (long)R * rb_l;                  // the first region of a stage
+  const long code_panel = (long)R * rb_l;  // stage stride of the codes
   const long comp_panel = (long)R * 64;
   const long scale_panel = (long)R * C::SBL;
   uint32_t voff[C::NIMAX];
@@ -173,16 +159,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     const int gr = min(r0 + r, rmax);  // ragged edge: clamped rows are never stored
     voff[i] = (uint32_t)gr * (uint32_t)rb_l + (uint32_t)(cc * 16);
   }
-  // E3M2 pairs' second region: 32-byte rows, two 16-byte chunks each (no chunk swizzle: the
-  // layout already permutes the 8-byte pieces by row)
-  uint32_t voffQ[C::NQMAX > 0 ? C::NQMAX : 1];
-#pragma unroll
-  for (int i = 0; i < C::NQMAX; ++i) {
-    const int p = (C::NCW * i + cw) * 64 + lane;
-    voffQ[i] = (uint32_t)min(r0 + (p >> 1), rmax) * 32u + (uint32_t)((p & 1) * 16);
-  }
-  const int nq = xside ? C::NQA : C::NQB;
-  const int dst_q = xside ? C::OFF_QA : C::OFF_QB;
   // scale bytes: lane l of wave-instruction q covers row q*SRPI + l/SLPR, bytes 4*(l%SLPR)
   uint32_t voffS[C::SCMAX];
 #pragma unroll
@@ -200,19 +176,13 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
     // compensation panel st (columns past KC in the last panel are loaded and zeroed at use),
     // else code panel st - ncs
     const auto rs = comp ? panel_rsrc(gcomp + (long)st * comp_panel, comp_panel)
-                         : panel_rsrc(gcodes + (long)(st - ncs) * code_panel, code_bytes);
+                         : panel_rsrc(gcodes + (long)(st - ncs) * code_panel, code_panel);
 #pragma unroll
     for (int i = 0; i < C::NIMAX; ++i)
       if (i < ni) dma16(rs, voff[i], buf + dst_rows + (C::NCW * i + cw) * 1024);
-    // scales (and E3M2 second regions) are also issued for compensation stages, from stage 0, so
-    // every stage has the same number of loads per wave; with G=64 one scale panel serves two stages
+    // scales are also issued for compensation stages, from stage 0, so every stage has the same
+    // number of loads per wave; with G=64 one scale panel serves two stages
     const int ks = comp ? 0 : st - ncs;
-    if constexpr (C::P6) {
-      const auto rq = panel_rsrc(gcodes + (long)ks * code_panel + code_bytes, (long)R * 32);
-#pragma unroll
-      for (int i = 0; i < C::NQMAX; ++i)
-        if (i < nq) dma16(rq, voffQ[i], buf + dst_q + (C::NCW * i + cw) * 1024);
-    }
     const auto ss = panel_rsrc(gscale + (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel, scale_panel);
 #pragma unroll
     for (int i = 0; i < C::SCMAX; ++i)
@@ -224,33 +194,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   // class follow in a small branch of their own.
   constexpr int NIU = C::NIA < C::NIB ? C::NIA : C::NIB;
   constexpr int SCU = C::SCA < C::SCB ? C::SCA : C::SCB;
-  constexpr int NQU = C::NQA < C::NQB ? C::NQA : C::NQB;
   auto issue_main_uniform = [&](int st_req, lds_u8* __restrict__ buf) {
     const int ks = min(st_req, nst - 1) - ncs;
-    const auto rs = panel_rsrc(gcodes + (long)ks * code_panel, code_bytes);
+    const auto rs = panel_rsrc(gcodes + (long)ks * code_panel, code_panel);
 #pragma unroll
     for (int i = 0; i < NIU; ++i) dma16(rs, voff[i], buf + dst_rows + (C::NCW * i + cw) * 1024);
-    if constexpr (C::P6) {
-      const auto rq = panel_rsrc(gcodes + (long)ks * code_panel + code_bytes, (long)R * 32);
-#pragma unroll
-      for (int i = 0; i < NQU; ++i) dma16(rq, voffQ[i], buf + dst_q + (C::NCW * i + cw) * 1024);
-    }
     const auto ss = panel_rsrc(gscale + (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel, scale_panel);
 #pragma unroll
     for (int i = 0; i < SCU; ++i) dma4(ss, voffS[i], buf + dst_scale + (C::NCW * i + cw) * 256);
   };
   auto issue_main_extra = [&](int st_req, lds_u8* __restrict__ buf) {
     const int ks = min(st_req, nst - 1) - ncs;
-    const auto rs = panel_rsrc(gcodes + (long)ks * code_panel, code_bytes);
+    const auto rs = panel_rsrc(gcodes + (long)ks * code_panel, code_panel);
 #pragma unroll
     for (int i = NIU; i < C::NIMAX; ++i)
       if (i < ni) dma16(rs, voff[i], buf + dst_rows + (C::NCW * i + cw) * 1024);
-    if constexpr (C::P6) {
-      const auto rq = panel_rsrc(gcodes + (long)ks * code_panel + code_bytes, (long)R * 32);
-#pragma unroll
-      for (int i = NQU; i < C::NQMAX; ++i)
-        if (i < nq) dma16(rq, voffQ[i], buf + dst_q + (C::NCW * i + cw) * 1024);
-    }
     const auto ss = panel_rsrc(gscale + (long)(C::SB >= 4 ? ks : ks >> 1) * scale_panel, scale_panel);
 #pragma unroll
     for (int i = SCU; i < C::SCMAX; ++i)
@@ -292,21 +250,17 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   auto read_half = [&](int st, int hf, Frag& f, bool comp_stage) {
     const lds_u8* __restrict__ As = smem + (st % NS) * C::STAGE;
     const lds_u8* __restrict__ Bs = As + C::OFF_B;
-    const lds_u8* __restrict__ QAs = As + C::OFF_QA;
-    const lds_u8* __restrict__ QBs = As + C::OFF_QB;
     if (COMP && comp_stage) {
       const bool valid = 32 * st + 16 * hf + 8 * h < KC;  // chunks past KC are zero operands
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         const v4i t = lds4(As + arow[i] * 64 + swz<64>(arow[i], 2 * hf + h) * 16);
         f.alo[0][i] = valid ? t : v4i{0, 0, 0, 0};
-        if constexpr (C::P6) f.ahi[0][i] = v4i{0, 0, 0, 0};  // unused here; keeps the fragment in registers
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         const v4i t = lds4(Bs + brow[j] * 64 + swz<64>(brow[j], 2 * hf + h) * 16);
         f.blo[0][j] = valid ? t : v4i{0, 0, 0, 0};
-        if constexpr (C::P6) f.bhi[0][j] = v4i{0, 0, 0, 0};
       }
       // the fragment slots a compensation half does not use are zeroed too: a fragment written
       // on every path stays in registers (otherwise it goes through scratch at the hand-over
@@ -333,11 +287,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
           } else {
             f.alo[sm][i] = lds4(As + r * 64 + swz<64>(r, 2 * m + h) * 16);
           }
-        } else if constexpr (FA == kFp6) {
-          // block 2m+h's 24-byte fragment: 16 bytes from the first region, 8 from the second
-          f.alo[sm][i] = lds4(As + r * 64 + swz<64>(r, 2 * m + h) * 16);
-          const v2i d = lds2(QAs + r * 32 + 8 * ((2 * m + h) ^ (((r >> 1) ^ (r >> 3)) & 3)));
-          f.ahi[sm][i] = v4i{d[0], d[1], 0, 0};
         } else {
           f.alo[sm][i] = lds4(As + r * 128 + swz<128>(r, 4 * m + h) * 16);
           f.ahi[sm][i] = lds4(As + r * 128 + swz<128>(r, 4 * m + 2 + h) * 16);
@@ -353,10 +302,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
           } else {
             f.blo[sm][j] = lds4(Bs + r * 64 + swz<64>(r, 2 * m + h) * 16);
           }
-        } else if constexpr (FB == kFp6) {
-          f.blo[sm][j] = lds4(Bs + r * 64 + swz<64>(r, 2 * m + h) * 16);
-          const v2i d = lds2(QBs + r * 32 + 8 * ((2 * m + h) ^ (((r >> 1) ^ (r >> 3)) & 3)));
-          f.bhi[sm][j] = v4i{d[0], d[1], 0, 0};
         } else {
           f.blo[sm][j] = lds4(Bs + r * 128 + swz<128>(r, 4 * m + h) * 16);
           f.bhi[sm][j] = lds4(Bs + r * 128 + swz<128>(r, 4 * m + 2 + h) * 16);
@@ -486,7 +431,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm(
   // read per fragment and MFMA), scale reads, uniform loads
   constexpr int NM_H = C::TM * C::TN * NSH;
   constexpr int ND_H = (C::TM * (FA != kFp4 ? 2 : 1) + C::TN * (FB != kFp4 ? 2 : 1)) * NSH;
-  constexpr int NV_H = NIU + SCU + NQU;
+  constexpr int NV_H = NIU + SCU;
   for (; st < nst; ++st) {
     lds_u8* const nb = smem + ((st + NS - 1) % NS) * C::STAGE;
     issue_main_uniform(st + NS - 1, nb);
