@@ -449,10 +449,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   // E3M2 pairs: each operand region is read through one descriptor over all its panels, fixed for
   // the loop, at a scalar offset that advances one panel per stage (the range check includes it),
   // and the loop is unrolled over the NS ring buffers so that a stage's LDS addresses are constants.
+  // Descriptor sizes and offsets are 32-bit: operands of 2 GiB or more take the general stage path.
   if constexpr (C::P6) {
-    if (st + NS - 1 < nst) {
+    const long npan = H / 128;
+    const bool fits = npan * S * C::CP < 0x80000000L && npan * N * C::CP < 0x80000000L;
+    if (fits && st + NS - 1 < nst) {
       const uint32_t k0 = (uint32_t)(st + NS - 1 - ncs);  // the code panel of the first stage loaded here
-      const long npan = H / 128;
       const uint32_t dX = (uint32_t)(S * C::CP), dW = (uint32_t)(N * C::CP);
       const auto rX = panel_rsrc(QX, npan * dX), rW = panel_rsrc(QW, npan * dW);
       const auto rXQ = panel_rsrc(QX + S * 64, npan * dX - S * 64), rWQ = panel_rsrc(QW + N * 64, npan * dW - N * 64);
