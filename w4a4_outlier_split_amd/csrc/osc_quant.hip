@@ -34,6 +34,192 @@ __device__ __forceinline__ us2 as_us2(uint32_t w) { return __builtin_bit_cast(us
 __device__ __forceinline__ uint32_t as_u32(us2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
 
+// ---- E3M2 pairs (G = 16 pairs carried by one scale per 32 elements)
+// E2M1 code c (at its 16-group's scale code) -> E3M2 code of the same value at the pair's scale
+// code, t = s_group - E_pair <= 2: the value 1.m * 2^p (p = -1 for 0.5) lands at exponent q = p + t;
+// q >= -2 is a normal E3M2 number, below that it is a multiple of 1/16 rounded to nearest, ties to
+// the even code (only when the pair's scale codes differ by more than 5).
+__device__ __forceinline__ uint32_t e2m1_to_e3m2(uint32_t c, int t) {
+  // selects only (no early return): the compiler keeps it branch-free
+  const uint32_t sign = (c & 8u) << 2;
+  const int mu = c & 7;
+  const int p = mu == 1 ? -1 : (mu >> 1) - 1;
+  const int m = mu == 1 ? 0 : (mu & 1);
+  const int q = p + t;
+  const uint32_t normal = (uint32_t)(((q + 3) << 2) | (m << 1));
+  const int units = q == -3 ? 2 + m : q == -4 ? (m ? 2 : 1) : q == -5 ? m : 0;  // of 1/16
+  const uint32_t mag = mu == 0 ? 0u : q >= -2 ? normal : (uint32_t)units;
+  return sign | mag;
+}
+
+// 8 E2M1 codes (one dword, code i in nibble i) at shift t = s_group - E_pair <= 2 -> their E3M2
+// codes, 48 bits: code i at bits [6i, 6i+6) of lo (bits 0..31) | hi16 << 32.
+__device__ __forceinline__ void e3m2_8(uint32_t codes4, int t, uint32_t& lo, uint32_t& hi16) {
+  lo = 0, hi16 = 0;
+  if (t >= -1) {
+    // groups within 3 scale codes of each other: every nonzero magnitude lands on a normal E3M2
+    // number, code = base(mu) + 4t with base = 8 for 0.5 and 2 mu + 8 above -- four codes per
+    // dword, one byte each (a byte permute looks up the base)
+    auto bytes = [](uint32_t n) {  // 4 nibbles -> 4 bytes
+      return (n & 0xFu) | ((n & 0xF0u) << 4) | ((n & 0xF00u) << 8) | ((n & 0xF000u) << 12);
+    };
+    auto conv = [&](uint32_t e) {
+      const uint32_t mu = e & 0x07070707u;
+      const uint32_t base = __builtin_amdgcn_perm(0x16141210u, 0x0E0C0800u, mu);
+      const uint32_t nz = __builtin_amdgcn_perm(0x01010101u, 0x01010100u, mu);
+      const uint32_t c = t >= 0 ? base + nz * (uint32_t)(4 * t) : base - nz * 4u;
+      const uint32_t x = c | ((e & 0x08080808u) << 2);  // sign bit 3 -> 5
+      return (x & 0x3Fu) | ((x >> 2) & 0xFC0u) | ((x >> 4) & 0x3F000u) | ((x >> 6) & 0xFC0000u);  // 4 x 6 bits
+    };
+    const uint32_t a = conv(bytes(codes4 & 0xFFFFu)), b = conv(bytes(codes4 >> 16));
+    lo = a | (b << 24);
+    hi16 = b >> 8;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c6 = e2m1_to_e3m2((codes4 >> (4 * i)) & 15u, t);
+      const int bit = 6 * i;
+      if (bit + 6 <= 32) {
+        lo |= c6 << bit;
+      } else if (bit >= 32) {
+        hi16 |= c6 << (bit - 32);
+      } else {
+        lo |= c6 << bit;
+        hi16 |= c6 >> (32 - bit);
+      }
+    }
+  }
+}
+
+// The gated path's E3M2 pairs (8 channels per lane): the lane's 8 E2M1 codes (one dword, channel 2i
+// in the low nibble of byte i) -> the pair's E3M2 codes and its stores.  The four lanes of a quad hold one 32-element block (lanes 0-1: 16-group
+// 2b, lanes 2-3: 2b+1); lane q's 8 codes are bits [48q, 48q+48) of the block's 24-byte fragment.
+__device__ __forceinline__ void pair_store(uint32_t codes4, int sx, int r, int col0, int rows,
+                                           uint8_t* __restrict__ Q, uint8_t* __restrict__ SC) {
+  const int sx_other = __builtin_amdgcn_update_dpp(0, sx, 0x4E, 0xF, 0xF, false);  // the other 16-group
+  const int hi = sx > sx_other ? sx : sx_other;
+  const int E = hi > 2 ? hi - 2 : 0;
+  const int t = sx - E;
+  uint32_t lo, hi16;  // 48 bits: lo = bits 0..31, hi16 = bits 32..47
+  e3m2_8(codes4, t, lo, hi16);
+  // every lane of the quad learns the four 48-bit pieces
+  const uint32_t lo0 = __builtin_amdgcn_update_dpp(0, lo, 0x00, 0xF, 0xF, false);
+  const uint32_t lo1 = __builtin_amdgcn_update_dpp(0, lo, 0x55, 0xF, 0xF, false);
+  const uint32_t lo2 = __builtin_amdgcn_update_dpp(0, lo, 0xAA, 0xF, 0xF, false);
+  const uint32_t lo3 = __builtin_amdgcn_update_dpp(0, lo, 0xFF, 0xF, 0xF, false);
+  const uint32_t h0 = __builtin_amdgcn_update_dpp(0, hi16, 0x00, 0xF, 0xF, false);
+  const uint32_t h1 = __builtin_amdgcn_update_dpp(0, hi16, 0x55, 0xF, 0xF, false);
+  const uint32_t h2 = __builtin_amdgcn_update_dpp(0, hi16, 0xAA, 0xF, 0xF, false);
+  const uint32_t h3 = __builtin_amdgcn_update_dpp(0, hi16, 0xFF, 0xF, 0xF, false);
+  const int q = (col0 >> 3) & 3;     // lane in the quad
+  const int b = (col0 & 127) >> 5;   // block in the stage
+  const long stage = (long)(col0 >> 7) * rows * 96;
+  // fragment dwords 0..3 (one per lane) -> the first R x 64 bytes of the stage
+  const uint32_t d = q == 0 ? lo0 : q == 1 ? (h0 | (lo1 << 16)) : q == 2 ? ((lo1 >> 16) | (h1 << 16)) : lo2;
+  __builtin_nontemporal_store(d, reinterpret_cast<uint32_t*>(Q + stage + (long)r * 64 + b * 16 + q * 4));
+  // dwords 4, 5 (lanes 0, 1) -> the R x 32 bytes after them, block position XOR-permuted by row
+  if (q < 2) {
+    const uint32_t e = q == 0 ? (h2 | (lo3 << 16)) : ((lo3 >> 16) | (h3 << 16));
+    __builtin_nontemporal_store(
+        e, reinterpret_cast<uint32_t*>(Q + stage + (long)rows * 64 + (long)r * 32 + 8 * (b ^ (((r >> 1) ^ (r >> 3)) & 3)) + q * 4));
+  }
+  // one scale byte per block, at the G = 32 scale layout
+  if (q == 0) {
+    const int k32 = col0 >> 5;
+    SC[((long)(k32 >> 2) * rows + r) * 4 + (k32 & 3)] = (uint8_t)E;
+  }
+}
+
+// One 16-byte chunk c (8 bf16 of one row): extraction, group scale, encoding, tiled stores.
+template <int G, int FMT, int MODE, int M>
+__device__ __forceinline__ void quant_chunk(u4 v, int r, int col0, int rows, const TableArg& tab,
+                                            uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
+                                            uint16_t* __restrict__ side) {
+  constexpr int LPG = G / 8;  // lanes per group
+  const int k = col0 / G;
+  const int q = (col0 % G) >> 3;
+  constexpr int SPG = G == 16 ? 8 : 4;  // groups per scale panel
+  const long code_at = ((long)(col0 >> 7) * rows + r) * 16 + ((col0 & 127) >> 3);  // in 4 / 8-byte units
+  const long scale_at = ((long)(k / SPG) * rows + r) * SPG + k % SPG;
+  const uint32_t x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];  // as loaded
+  uint32_t w0 = x0, w1 = x1, w2 = x2, w3 = x3;                  // with the listed slots zeroed
+
+  if (MODE != kNoTable) {
+    // entries k*m .. k*m+m-1 of the table list distinct channels of group k (or -1); entry e goes
+    // to compensation column k*m + e, written by the lane holding the channel (or lane 0 of the
+    // group, as +0, for -1)
+#pragma unroll
+    for (int e = 0; e < M; ++e) {
+      {
+        const int ent = tab.v[k * M + e];
+        const bool own = ent >= 0 && (ent >> 3) == q;
+        uint32_t val = 0;
+        if (own) {
+          const int c = ent & 7;
+          const uint32_t word = (c >> 1) == 0 ? x0 : (c >> 1) == 1 ? x1 : (c >> 1) == 2 ? x2 : x3;
+          val = (c & 1) ? (word >> 16) : (word & 0xFFFFu);
+          if (MODE == kExtractZero) {
+            const uint32_t keep = (c & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            w0 = (c >> 1) == 0 ? (w0 & keep) : w0;
+            w1 = (c >> 1) == 1 ? (w1 & keep) : w1;
+            w2 = (c >> 1) == 2 ? (w2 & keep) : w2;
+            w3 = (c >> 1) == 3 ? (w3 & keep) : w3;
+          }
+        }
+        const int col = k * M + e;
+        if (own || (ent < 0 && q == 0)) side[((long)(col >> 5) * rows + r) * 32 + (col & 31)] = (uint16_t)val;
+      }
+    }
+  }
+
+  // group amax over the magnitude bits
+  us2 mx = __builtin_elementwise_max(as_us2(w0 & 0x7FFF7FFFu), as_us2(w1 & 0x7FFF7FFFu));
+  mx = __builtin_elementwise_max(mx, as_us2(w2 & 0x7FFF7FFFu));
+  mx = __builtin_elementwise_max(mx, as_us2(w3 & 0x7FFF7FFFu));
+  int amax = mx.x > mx.y ? mx.x : mx.y;
+  // group max across the LPG adjacent lanes with DPP lane swaps: neighbours (quad_perm 1,0,3,2),
+  // pairs (quad_perm 2,3,0,1), then the two quads of an 8-lane row half (half-row mirror)
+  amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0xB1, 0xF, 0xF, false));
+  if constexpr (LPG >= 4) amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0x4E, 0xF, 0xF, false));
+  if constexpr (LPG >= 8) amax = max(amax, __builtin_amdgcn_update_dpp(0, amax, 0x141, 0xF, 0xF, false));
+  const int E = amax >> 7;
+  const int sx = FMT != OSC_MXFP8 ? (E > 2 ? E - 2 : 0) : (E > 8 ? E - 8 : 0);
+  if (FMT != OSC_FP6P && q == 0) SC[scale_at] = (uint8_t)sx;
+  const float scale = __builtin_bit_cast(float, (uint32_t)sx << 23);  // only the exponent field is used
+
+  if constexpr (FMT == OSC_FP6P) {
+    static_assert(G == 16, "E3M2 pairs carry two 16-groups");
+    uint32_t out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w0), scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w1), scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w2), scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w3), scale, 3);
+    pair_store(out, sx, r, col0, rows, Q, SC);
+  } else if (FMT == OSC_MXFP4) {
+    uint32_t out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w0), scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w1), scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w2), scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, as_bf2(w3), scale, 3);
+    __builtin_nontemporal_store(out, reinterpret_cast<uint32_t*>(Q) + code_at);
+  } else {
+    // saturate: |x| <= 448 * 2^e, i.e. exponent field sx + 8 with mantissa 0b1100000
+    const uint32_t lim = (((uint32_t)sx + 8u) << 7) | 0x60u;
+    const us2 lim2 = {(unsigned short)lim, (unsigned short)lim};
+    w0 = (w0 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w0 & 0x7FFF7FFFu), lim2));
+    w1 = (w1 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w1 & 0x7FFF7FFFu), lim2));
+    w2 = (w2 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w2 & 0x7FFF7FFFu), lim2));
+    w3 = (w3 & 0x80008000u) | as_u32(__builtin_elementwise_min(as_us2(w3 & 0x7FFF7FFFu), lim2));
+    s2 o0 = {0, 0}, o1 = {0, 0};
+    o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, as_bf2(w0), scale, false);
+    o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, as_bf2(w1), scale, true);
+    o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, as_bf2(w2), scale, false);
+    o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, as_bf2(w3), scale, true);
+    const u2 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1)};
+    __builtin_nontemporal_store(o, reinterpret_cast<u2*>(Q) + code_at);
+  }
+}
+
 // ------------------------------------------------------------------ MLP glue
 // In a Qwen3-shaped MLP block the down-projection reads h = silu(gate) * up, the two halves of
 // the up-projection's bf16 output (not an OSC step; the quantization of W2's input then follows
@@ -91,12 +277,11 @@ __global__ __launch_bounds__(256) void k_swiglu(const u4* __restrict__ GU, int r
   }
 }
 
-// The quantization kernel.  The block a lane holds is two 16-groups (G = 16 and the pairs), one
-// group (G = 32), or half of one (G = 64: the halves sit in neighbouring lanes of the same row and
-// meet in one DPP lane swap for the amax).  Pairs re-encode to E3M2 with the conversion
-// instructions: each group's E2M1 codes back to bf16 at the relative scale, then all 32 values to
-// E3M2 in one instruction.
-// GLU: X holds rows of 2H bf16 (gate | up) and the row quantized is h = glu(gate, up) of H.
+// The quantization kernel (activations and weights without the MLP glue).  The block a lane holds
+// is two 16-groups (G = 16 and the pairs), one group (G = 32), or half of one (G = 64: the halves
+// sit in neighbouring lanes of the same row and meet in one DPP lane swap for the amax).  Pairs
+// re-encode to E3M2 with the conversion instructions: each group's E2M1 codes back to bf16 at the
+// relative scale, then all 32 values to E3M2 in one instruction.
 constexpr int kBlkRows = 16;
 
 // dword d (lane-varying, 0 <= d < N) of the N words w[0..N), by a binary tree of selects on d's bits
@@ -114,7 +299,7 @@ __device__ __forceinline__ uint32_t pick(const uint32_t* w, int d) {
   return t[0];
 }
 
-template <int G, int FMT, int MODE, int M, bool GLU>
+template <int G, int FMT, int MODE, int M>
 __global__ __launch_bounds__(256) void k_quant_blk(const u4* __restrict__ X, int rows, int H, TableArg tab,
                                                    uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
                                                    uint16_t* __restrict__ side) {
@@ -132,26 +317,12 @@ __global__ __launch_bounds__(256) void k_quant_blk(const u4* __restrict__ X, int
   if (r >= rows) return;  // a row's four lanes leave together: the G = 64 swap stays inside a row
   const int col0 = p * 128 + b * 32;
   uint32_t x[16], v[16];  // dword j: channels col0 + 2j (low half), 2j + 1
-  if constexpr (GLU) {
-    const u4* g = X + (long)r * (H >> 2) + (col0 >> 3);
-    const u4* u = g + (H >> 3);
-    u4 gv[4], uv[4];
+  const u4* src = X + (long)r * (H >> 3) + (col0 >> 3);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) gv[c] = __builtin_nontemporal_load(g + c), uv[c] = __builtin_nontemporal_load(u + c);
+  for (int c = 0; c < 4; ++c) {
+    const u4 t = src[c];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u4 t = glu_chunk(gv[c], uv[c]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * c + i] = v[4 * c + i] = t[i];
-    }
-  } else {
-    const u4* src = X + (long)r * (H >> 3) + (col0 >> 3);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u4 t = src[c];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * c + i] = v[4 * c + i] = t[i];
-    }
+    for (int i = 0; i < 4; ++i) x[4 * c + i] = v[4 * c + i] = t[i];
   }
   if (MODE != kNoTable) {
     // entry e of group k goes to compensation column k*m + e (+0 for -1), written by the lane that
@@ -278,19 +449,86 @@ __global__ __launch_bounds__(256) void k_quant_blk(const u4* __restrict__ X, int
   }
 }
 
-template <int G, int FMT, int MODE, bool GLU>
+template <int G, int FMT, int MODE>
 hipError_t launch_blk_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC,
                         uint16_t* sd, unsigned grid, hipStream_t st) {
   switch (m) {
-    case 1: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 1, GLU>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
-    case 2: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 2, GLU>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
-    default: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 3, GLU>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 1: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 2: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 2>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    default: hipLaunchKernelGGL((k_quant_blk<G, FMT, MODE, 3>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
   }
   return hipGetLastError();
 }
 
-// mode: the table mode (kNoTable for E4M3); the gated input feeds activations only (no copy mode)
-template <int G, int FMT, bool GLU>
+// The quantization of h = glu(gate, up) for a gated MLP's down-projection: X holds rows of 2H bf16
+// (gate | up).  The glue is long vector arithmetic, so this kernel keeps 8 channels per lane (few
+// registers, many resident wavefronts): a wavefront owns 8 rows x one 128-channel panel, 16 lanes
+// covering a row's 256 bytes of h per load instruction and 4 rows at once; groups are G/8 adjacent
+// lanes, their amax reduced across lanes with DPP swaps (quant_chunk).
+constexpr int kRowsPerWave = 8;
+
+template <int G, int FMT, int MODE, int M>
+__global__ __launch_bounds__(256) void k_quant_glu(const u4* __restrict__ X, int rows, int H, TableArg tab,
+                                                   uint8_t* __restrict__ Q, uint8_t* __restrict__ SC,
+                                                   uint16_t* __restrict__ side) {
+  const int npan = H >> 7;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave -> (row block, panel), panel fastest
+  const int rb = w / npan;
+  const int p = w - rb * npan;
+  if (rb * kRowsPerWave >= rows) return;  // whole wavefront past the last row
+  const int lane = threadIdx.x & 63;
+  const int cc = lane & 15;  // chunk of the panel row
+  const int col0 = p * 128 + cc * 8;
+  const int r0 = rb * kRowsPerWave + (lane >> 4);
+  // rows past the end are skipped by whole 16-lane row segments, so a group's lanes agree
+  constexpr int U = kRowsPerWave / 4;
+  u4 vg[U], vu[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = r0 + 4 * u;
+    if (r < rows) {
+      const u4* row = X + (long)r * (H >> 2);
+      vg[u] = __builtin_nontemporal_load(row + (col0 >> 3));
+      vu[u] = __builtin_nontemporal_load(row + ((H + col0) >> 3));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = r0 + 4 * u;
+    if (r < rows) quant_chunk<G, FMT, MODE, M>(glu_chunk(vg[u], vu[u]), r, col0, rows, tab, Q, SC, side);
+  }
+}
+
+template <int G, int FMT, int MODE>
+hipError_t launch_glu_m(const u4* x, int rows, int H, int m, const TableArg& t, uint8_t* q, uint8_t* SC,
+                        uint16_t* sd, unsigned grid, hipStream_t st) {
+  switch (m) {
+    case 1: hipLaunchKernelGGL((k_quant_glu<G, FMT, MODE, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    case 2: hipLaunchKernelGGL((k_quant_glu<G, FMT, MODE, 2>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+    default: hipLaunchKernelGGL((k_quant_glu<G, FMT, MODE, 3>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd); break;
+  }
+  return hipGetLastError();
+}
+
+template <int G, int FMT>
+hipError_t dispatch_glu(const void* X, int rows, int H, int m, const TableArg* tab, int mode, void* Q, uint8_t* SC,
+                        void* side, hipStream_t st) {
+  const long waves = (long)((rows + kRowsPerWave - 1) / kRowsPerWave) * (H >> 7);
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const u4* x = static_cast<const u4*>(X);
+  uint8_t* q = static_cast<uint8_t*>(Q);
+  uint16_t* sd = static_cast<uint16_t*>(side);
+  static const TableArg empty = {};
+  const TableArg& t = tab ? *tab : empty;
+  if constexpr (FMT != OSC_MXFP8)
+    if (mode == kExtractZero) return launch_glu_m<G, FMT, kExtractZero>(x, rows, H, m, t, q, SC, sd, grid, st);
+  if (mode != kNoTable) return hipErrorInvalidValue;  // the glue feeds activations only (no copy mode)
+  hipLaunchKernelGGL((k_quant_glu<G, FMT, kNoTable, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
+  return hipGetLastError();
+}
+
+// mode: the table mode (kNoTable for E4M3)
+template <int G, int FMT>
 hipError_t dispatch_blk(const void* X, int rows, int H, int m, const TableArg* tab, int mode, void* Q, uint8_t* SC,
                         void* side, hipStream_t st) {
   const long waves = (long)((rows + kBlkRows - 1) / kBlkRows) * (H >> 7);
@@ -301,12 +539,11 @@ hipError_t dispatch_blk(const void* X, int rows, int H, int m, const TableArg* t
   static const TableArg empty = {};
   const TableArg& t = tab ? *tab : empty;
   if constexpr (FMT != OSC_MXFP8) {
-    if (mode == kExtractZero) return launch_blk_m<G, FMT, kExtractZero, GLU>(x, rows, H, m, t, q, SC, sd, grid, st);
-    if constexpr (!GLU)
-      if (mode == kCopyOnly) return launch_blk_m<G, FMT, kCopyOnly, GLU>(x, rows, H, m, t, q, SC, sd, grid, st);
+    if (mode == kExtractZero) return launch_blk_m<G, FMT, kExtractZero>(x, rows, H, m, t, q, SC, sd, grid, st);
+    if (mode == kCopyOnly) return launch_blk_m<G, FMT, kCopyOnly>(x, rows, H, m, t, q, SC, sd, grid, st);
   }
   if (mode != kNoTable) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_quant_blk<G, FMT, kNoTable, 1, GLU>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
+  hipLaunchKernelGGL((k_quant_blk<G, FMT, kNoTable, 1>), dim3(grid), dim3(256), 0, st, x, rows, H, t, q, SC, sd);
   return hipGetLastError();
 }
 
@@ -314,11 +551,18 @@ template <int G, bool GLU>
 hipError_t dispatch_fmt(const void* X, int rows, int H, int m, const TableArg* tab, int mode, osc_fmt fmt, void* Q,
                         uint8_t* SC, void* side, hipStream_t st) {
   if (fmt == OSC_FP6P) {
-    if constexpr (G == 16) return dispatch_blk<16, OSC_FP6P, GLU>(X, rows, H, m, tab, mode, Q, SC, side, st);
+    if constexpr (G == 16) {
+      if constexpr (GLU) return dispatch_glu<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
+      return dispatch_blk<16, OSC_FP6P>(X, rows, H, m, tab, mode, Q, SC, side, st);
+    }
     return hipErrorInvalidValue;  // E3M2 pairs exist for G = 16 only
   }
-  if (fmt == OSC_MXFP4) return dispatch_blk<G, OSC_MXFP4, GLU>(X, rows, H, m, tab, mode, Q, SC, side, st);
-  return dispatch_blk<G, OSC_MXFP8, GLU>(X, rows, H, m, tab, mode, Q, SC, side, st);
+  if constexpr (GLU) {
+    if (fmt == OSC_MXFP4) return dispatch_glu<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
+    return dispatch_glu<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
+  }
+  if (fmt == OSC_MXFP4) return dispatch_blk<G, OSC_MXFP4>(X, rows, H, m, tab, mode, Q, SC, side, st);
+  return dispatch_blk<G, OSC_MXFP8>(X, rows, H, m, tab, mode, Q, SC, side, st);
 }
 
 // ------------------------------------------------------------------ table builder
