@@ -1,4 +1,5 @@
-// Dual-path OSC GEMM for MXFP4 activations and weights at G = 32 / 64 (OSC page
+// Dual-path OSC GEMM for MXFP4 activations and weights at G = 32 / 64, and for the G = 16 pairs
+// carried as E3M2 under one scale per 32 elements (OSC page
 // "W4A4量化技术：OSC框架如何实现高效LLM部署", §3.2: Y = (Q_X ⊗ Q_W)·S + B·W_L; §3.3: the 4-bit and
 // the 16-bit operand streams are consumed by one kernel into the same accumulators).
 //

@@ -52,8 +52,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
-// MXFP4 activations and weights at G = 32 / 64 on 16x16 MFMA blocks (the prefill path of
-// launch_gemm for that format).
+// MXFP4 activations and weights at G = 32 / 64, and the E3M2 pairs, on 32x32 scaled MFMA blocks
+// (the prefill path of launch_gemm for those formats).
 hipError_t launch_gemm_mx4(const GemmArgs& a, hipStream_t st);
 
 // S <= 32 rows: the skinny-S kernel (one 32-column block per workgroup, K split over its waves).
