@@ -81,5 +81,25 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, lds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, off, 0, 0, 0);
 }
 
+// The tile (row block tm, column block tn) of workgroup b in a grid of ntm x ntn tiles, XCD-aware:
+// workgroup b runs on XCD b % 8, and each XCD takes a block of the grid, M fastest inside it.
+// xblk = 0: the blocks are contiguous runs of T/8 tiles in M-fastest order (every workgroup in
+// turn when T is not a multiple of 8); else xblk = bm << 4 | log2(gm): the grid is cut into gm
+// blocks of bm tiles along M times 8 / gm blocks along N (xcd_blocks chooses).
+__device__ __forceinline__ void xcd_tile(int b, int ntm, int ntn, int xblk, int& tm, int& tn) {
+  if (xblk == 0) {
+    const int total = ntm * ntn;
+    const int tile = (total & 7) == 0 ? (b & 7) * (total >> 3) + (b >> 3) : b;
+    tm = tile % ntm;
+    tn = tile / ntm;
+  } else {
+    const int bm = xblk >> 4, sh = xblk & 15, bn = (ntn << sh) >> 3;
+    const int x = b & 7, j = b >> 3;
+    const int jm = j % bm;
+    tm = (x & ((1 << sh) - 1)) * bm + jm;
+    tn = (x >> sh) * bn + (j - jm) / bm;
+  }
+}
+
 }  // namespace
 }  // namespace osc

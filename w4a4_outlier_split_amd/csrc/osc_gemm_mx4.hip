@@ -109,25 +109,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
-  // XCD-aware tile order (xcd_blocks below): workgroup w runs on XCD w % 8, and each XCD takes a
-  // block of the tile grid, M fastest inside it.  xblk = 0: the blocks are contiguous runs of T/8
-  // tiles in M-fastest order; else xblk = bm << 4 | log2(gm): the grid is cut into gm blocks of bm
-  // tiles along M times 8 / gm blocks along N.
+  // XCD-aware tile order (xcd_tile, with the blocks xcd_blocks chooses on the host)
   const int ntm = (S + BM - 1) / BM;
   const int ntn = (N + BN - 1) / BN;
-  int m0, n0;
-  if (xblk == 0) {
-    const int total = ntm * ntn;
-    const int tile = (total & 7) == 0 ? (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-    m0 = (tile % ntm) * BM;
-    n0 = (tile / ntm) * BN;
-  } else {
-    const int bm = xblk >> 4, sh = xblk & 15, bn = (ntn << sh) >> 3;
-    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int jm = j % bm;
-    m0 = ((x & ((1 << sh) - 1)) * bm + jm) * BM;
-    n0 = ((x >> sh) * bn + (j - jm) / bm) * BN;
-  }
+  int tm, tn;
+  xcd_tile(blockIdx.x, ntm, ntn, xblk, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
 
   const int nks = H / 128;
   const int ncs = COMP ? (KC + 31) / 32 : 0;
@@ -589,28 +576,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
             }
         }
       }
-}
-
-// The XCD blocks of a grid of ntm x ntn tiles of BM x BN: by default each XCD takes a contiguous
-// run of T/8 tiles in M-fastest order.  The grid can instead be cut into 8 blocks of bm x bn tiles
-// shaped so that the activation and weight rows an XCD's L2 fetches per stage (bm * BM + bn * BN)
-// are fewest; that shape is taken when it cuts those rows by a fifth or more (measured: the QKV
-// grid, 9 % fewer rows, ran 0.8 % slower with it; 33-43 % fewer ran 1.6-7 % faster).  Returns the
-// kernel's xblk argument.
-int xcd_blocks(int ntm, int ntn, int BM, int BN) {
-  const int total = ntm * ntn;
-  if ((total & 7) != 0) return 0;
-  const int run = total >> 3;
-  const long run_rows = (long)(run < ntm ? run : ntm) * BM + (long)((run + ntm - 1) / ntm) * BN;
-  long best = 0;
-  int arg = 0;
-  for (int sh = 0; sh <= 3; ++sh) {  // gm = 2^sh blocks along M, 8 / gm along N
-    const int gm = 1 << sh, gn = 8 >> sh;
-    if (ntm % gm || ntn % gn) continue;
-    const long rows = (long)(ntm / gm) * BM + (long)(ntn / gn) * BN;
-    if (arg == 0 || rows < best) best = rows, arg = (ntm / gm) << 4 | sh;
-  }
-  return arg != 0 && best * 5 <= run_rows * 4 ? arg : 0;
 }
 
 template <int G, int FM, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>

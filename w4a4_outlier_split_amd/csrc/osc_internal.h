@@ -52,6 +52,10 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
+// The prefill GEMMs' XCD tile blocks for a grid of ntm x ntn tiles of BM x BN (the kernels'
+// xblk argument; see xcd_tile in osc_device.h).
+int xcd_blocks(int ntm, int ntn, int BM, int BN);
+
 // MXFP4 activations and weights at G = 32 / 64, and the E3M2 pairs, on 32x32 scaled MFMA blocks
 // (the prefill path of launch_gemm for those formats).
 hipError_t launch_gemm_mx4(const GemmArgs& a, hipStream_t st);
