@@ -15,10 +15,10 @@
 // global -> LDS by LDS-DMA into a ring of NS buffers, NS - 1 stages ahead.  One barrier per stage
 // splits it into its two K halves: half 0 before the barrier, half 1 after it, while the next
 // stage's first-half fragments and scales are read; compensation and main stages share that
-// schedule.  A stage's loads (row blocks and the two sides' scale dwords) are dealt out to all
-// waves alike, the slots left over going through a resource with no records, and past the last
-// stage every wave keeps issuing such loads: the stage body has no branch and every wait is the
-// same count.
+// schedule.  A stage's loads (row blocks and the two sides' scale dwords) are dealt out to the
+// waves in turn; a wave whose last slot would stay empty runs a copy of the body with one load
+// fewer per stage, and past the last stage every wave keeps issuing its loads through resources
+// with no records: each stage body has no branch and each wave waits on one count throughout.
 #include <type_traits>
 
 #include "osc_device.h"
@@ -50,8 +50,8 @@ struct Cfg4 {
   // The loads of one stage, each one LDS-DMA of 64 lanes x 16 bytes: XB blocks of 16 activation
   // rows (64 bytes each), WB blocks of 16 weight rows, for E3M2 pairs XQ / WQ blocks of 32 rows of
   // the 32-byte second region, the activation scale dwords of the tile (4 rows per lane), the
-  // weight scale dwords.  Load g of the stage is issued by wave g % NW; every wave issues D of them,
-  // the slots past the last load going through a resource with no records into a spare kilobyte.
+  // weight scale dwords.  Load g of the stage is issued by wave g % NW in its slot g / NW: D slots
+  // per wave, the waves whose slot D - 1 lies past the last load (kind kNone) issuing D - 1.
   static constexpr int XB = BM / 16, WB = BN / 16;
   static constexpr int XQ = P6 ? BM / 32 : 0, WQ = P6 ? BN / 32 : 0;
   static constexpr int NLOAD = XB + WB + XQ + WQ + 2;
@@ -79,8 +79,7 @@ struct Cfg4 {
   static constexpr int OFF_QB = OFF_QA + XQ * 1024;   // E3M2 pairs: weight second-region rows
   static constexpr int OFF_SA = OFF_QB + WQ * 1024;   // activation scale dwords (one per row)
   static constexpr int OFF_SB = OFF_SA + 1024;        // weight scale dwords
-  static constexpr int OFF_J = OFF_SB + 1024;         // spare kilobyte (the empty loads)
-  static constexpr int STAGE = OFF_J + 1024;
+  static constexpr int STAGE = OFF_SB + 1024;
   static constexpr int NS = (160 * 1024) / STAGE > 4 ? 4 : (160 * 1024) / STAGE;
   // LDS row stride of the bf16 output image: 8 bytes more than a row, so the 8-byte writes of 32
   // consecutive rows fall on 32 distinct bank pairs
@@ -93,15 +92,17 @@ struct Cfg4 {
   static_assert(G == 32 || (G == 64 && !P6), "scale bytes per stage");
 };
 
-template <int G, int FM, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
-    const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX, const uint8_t* __restrict__ Bc,
-    const uint8_t* __restrict__ QW, const uint8_t* __restrict__ SW, const uint8_t* __restrict__ WL,
-    void* __restrict__ Y, int S, int N, int H, int KC, int xblk) {
+// The body of k_gemm_mx4 for one wavefront.  SHORT: the wave's last load slot is empty in every
+// stage (kind kNone), so it issues DW = D - 1 loads per stage instead of D and waits on counts of
+// its own; the empty slot is not issued at all.
+template <int G, int FM, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N, bool SHORT>
+__device__ __forceinline__ void gemm_mx4_wave(
+    lds_u8* const smem, const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX,
+    const uint8_t* __restrict__ Bc, const uint8_t* __restrict__ QW, const uint8_t* __restrict__ SW,
+    const uint8_t* __restrict__ WL, void* __restrict__ Y, int S, int N, int H, int KC, int xblk) {
   using C = Cfg4<G, FM, BM, BN, WAVES_M, WAVES_N>;
   constexpr int NS = C::NS;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * C::STAGE];
-  lds_u8* const smem = (lds_u8*)smem_raw;
+  constexpr int DW = SHORT ? C::D - 1 : C::D;  // loads this wave issues per stage
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,9 +156,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
       voff[i] = (uint32_t)(r0 + 4 * lane) * 4u;
       dst[i] = k == C::kXScale ? C::OFF_SA : C::OFF_SB;
       ccol[i] = 0;
-    } else {
+    } else {  // an empty slot: never issued
       voff[i] = 0;
-      dst[i] = C::OFF_J;
+      dst[i] = 0;
       ccol[i] = 0;
     }
   }
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     // resource, as zeros
     const int climit = comp ? KC - 32 * s : 32;
 #pragma unroll
-    for (int i = 0; i < C::D; ++i) {
+    for (int i = 0; i < DW; ++i) {
       uintptr_t b;
       int n;
       const int sk = C::slot_kind(i);
@@ -351,9 +352,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     iss(st + NS - 1, smem + qn * C::STAGE);
     read_half(q, 1, f1, cs_t);
     mma(0, f0, sc, CS);
-    Interleave<0, NM_H, C::D, (C::P6 && !CS ? 2 : 1) * NF>::run();
+    Interleave<0, NM_H, DW, (C::P6 && !CS ? 2 : 1) * NF>::run();
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(NS - 2) * C::D>();
+    wait_vm<(NS - 2) * DW>();
     lds_barrier();
     if constexpr (!NCS) read_scales(q1, sr);
     read_half(q1, 0, f0, ncs_t);
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
   auto iss_comp = [&](int s, lds_u8* buf) __attribute__((always_inline)) { issue(T{}, s, buf); };
   auto iss_main = [&](int s, lds_u8* buf) __attribute__((always_inline)) { issue(F{}, s, buf); };
 
-  wait_vm<(NS - 2) * C::D>();  // stage 0 complete for this wave
+  wait_vm<(NS - 2) * DW>();  // stage 0 complete for this wave
   lds_barrier();
   const bool comp0 = COMP && ncs > 0;
   if (comp0)
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
     auto iss_fast = [&](auto odd_t) {
       return [&](int, lds_u8* buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::D; ++i) {
+        for (int i = 0; i < DW; ++i) {
           dma16(panel_rsrc((const uint8_t*)fp[i], fn[i]), voff[i], buf + dst[i]);
           fp[i] += decltype(odd_t)::value ? fsb[i] : fsa[i];
         }
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
       }
       auto iss6 = [&](int, lds_u8* buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::D; ++i) {
+        for (int i = 0; i < DW; ++i) {
           const int sk = C::slot_kind(i);
           if (sk == C::kXRows)
             dma16s(rX, voff[i], oX, buf + dst[i]);
@@ -576,6 +577,23 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
             }
         }
       }
+}
+
+// Each wave runs the body with its own load count: the waves whose last slot is empty skip it
+// (a uniform branch outside the stage loops, so each stage body stays one basic block).
+template <int G, int FM, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void k_gemm_mx4(
+    const uint8_t* __restrict__ QX, const uint8_t* __restrict__ SX, const uint8_t* __restrict__ Bc,
+    const uint8_t* __restrict__ QW, const uint8_t* __restrict__ SW, const uint8_t* __restrict__ WL,
+    void* __restrict__ Y, int S, int N, int H, int KC, int xblk) {
+  using C = Cfg4<G, FM, BM, BN, WAVES_M, WAVES_N>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[C::NS * C::STAGE];
+  lds_u8* const smem = (lds_u8*)smem_raw;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (C::kind(C::NW * (C::D - 1) + wave) == C::kNone)
+    gemm_mx4_wave<G, FM, COMP, YT, BM, BN, WAVES_M, WAVES_N, true>(smem, QX, SX, Bc, QW, SW, WL, Y, S, N, H, KC, xblk);
+  else
+    gemm_mx4_wave<G, FM, COMP, YT, BM, BN, WAVES_M, WAVES_N, false>(smem, QX, SX, Bc, QW, SW, WL, Y, S, N, H, KC, xblk);
 }
 
 template <int G, int FM, bool COMP, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
