@@ -593,11 +593,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.G != 16) return launch_gemm_mx4(a, st);  // osc_gemm_mx4.hip
     return pick_comp<kFp4, kFp4, 16>(a, st);
   }
-  // FP8 activations: no compensation path
-  if (a.wfmt == OSC_MXFP4) {
-    if (a.G == 32) return pick_nocomp<kFp8, kFp4, 32>(a, st);
-    return pick_nocomp<kFp8, kFp4, 64>(a, st);
-  }
+  // FP8 activations: no compensation path; with E2M1 weights on osc_gemm_mx4.hip
+  if (a.wfmt == OSC_MXFP4) return launch_gemm_mx4(a, st);
   if (a.G == 32) return pick_nocomp<kFp8, kFp8, 32>(a, st);
   return pick_nocomp<kFp8, kFp8, 64>(a, st);
 }

@@ -1,5 +1,6 @@
-// Dual-path OSC GEMM for MXFP4 activations and weights at G = 32 / 64, and for the G = 16 pairs
-// carried as E3M2 under one scale per 32 elements (OSC page
+// Dual-path OSC GEMM for MXFP4 activations and weights at G = 32 / 64, for the G = 16 pairs
+// carried as E3M2 under one scale per 32 elements, and for E4M3 activations with E2M1 weights
+// (the W2 fallback, §4: no compensation) (OSC page
 // "W4A4量化技术：OSC框架如何实现高效LLM部署", §3.2: Y = (Q_X ⊗ Q_W)·S + B·W_L; §3.3: the 4-bit and
 // the 16-bit operand streams are consumed by one kernel into the same accumulators).
 //
@@ -10,8 +11,9 @@
 //
 // Pipeline (per workgroup: a BM x BN tile of Y, WAVES_M x WAVES_N wavefronts, each a WTM x WTN
 // sub-tile = TM x TN blocks).  K is cut into stages: first ceil(KC / 32) compensation stages
-// (32 columns of B / W_L, bf16: v_mfma_f32_32x32x16_bf16), then H / 128 main stages (128 E2M1
-// codes: v_mfma_scale_f32_32x32x64_f8f6f4), each one 64-byte row per operand row, copied
+// (32 columns of B / W_L, bf16: v_mfma_f32_32x32x16_bf16), then H / 128 main stages (128 codes:
+// v_mfma_scale_f32_32x32x64_f8f6f4), each one 64-byte row per E2M1 row (128 bytes per E4M3 row,
+// 96 per E3M2 row in two regions), copied
 // global -> LDS by LDS-DMA into a ring of NS buffers, NS - 1 stages ahead.  One barrier per stage
 // splits it into its two K halves: half 0 before the barrier, half 1 after it, while the next
 // stage's first-half fragments and scales are read; compensation and main stages share that
@@ -44,6 +46,8 @@ struct RingFor {
 template <int G, int FM, int BM, int BN, int WAVES_M, int WAVES_N>
 struct Cfg4 {
   static constexpr bool P6 = FM == kFp6;         // E3M2 pairs (G = 16 carried by 32-wide scale blocks)
+  static constexpr bool A8 = FM == kFp8;         // E4M3 activations, E2M1 weights (the W2 fallback)
+  static constexpr int XR = A8 ? 128 : 64;       // bytes per activation row of a stage (first region)
   static constexpr int NW = WAVES_M * WAVES_N;  // wavefronts per workgroup
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 blocks per wavefront
@@ -52,7 +56,7 @@ struct Cfg4 {
   // the 32-byte second region, the activation scale dwords of the tile (4 rows per lane), the
   // weight scale dwords.  Load g of the stage is issued by wave g % NW in its slot g / NW: D slots
   // per wave, the waves whose slot D - 1 lies past the last load (kind kNone) issuing D - 1.
-  static constexpr int XB = BM / 16, WB = BN / 16;
+  static constexpr int XB = BM * XR / 1024, WB = BN / 16;
   static constexpr int XQ = P6 ? BM / 32 : 0, WQ = P6 ? BN / 32 : 0;
   static constexpr int NLOAD = XB + WB + XQ + WQ + 2;
   static constexpr int D = (NLOAD + NW - 1) / NW;  // loads per wave per stage
@@ -66,7 +70,8 @@ struct Cfg4 {
            : g == XB + WB + XQ + WQ + 1 ? kWScale
                                    : kNone;
   }
-  static constexpr int CP = P6 ? 96 : 64;  // bytes per row of a code panel (a stage of 128 channels)
+  // bytes per row of an activation / weight code panel (a stage of 128 channels)
+  static constexpr int CPX = P6 ? 96 : XR, CPW = P6 ? 96 : 64;
   // the kind of slot i when it is the same for every wave, else -1
   static constexpr int slot_kind(int i) {
     const int k = kind(NW * i);
@@ -74,8 +79,8 @@ struct Cfg4 {
       if (kind(NW * i + w) != k) return -1;
     return k;
   }
-  static constexpr int OFF_B = BM * 64;               // weight rows
-  static constexpr int OFF_QA = (BM + BN) * 64;       // E3M2 pairs: activation second-region rows
+  static constexpr int OFF_B = BM * XR;               // weight rows
+  static constexpr int OFF_QA = OFF_B + BN * 64;      // E3M2 pairs: activation second-region rows
   static constexpr int OFF_QB = OFF_QA + XQ * 1024;   // E3M2 pairs: weight second-region rows
   static constexpr int OFF_SA = OFF_QB + WQ * 1024;   // activation scale dwords (one per row)
   static constexpr int OFF_SB = OFF_SA + 1024;        // weight scale dwords
@@ -103,6 +108,7 @@ __device__ __forceinline__ void gemm_mx4_wave(
   using C = Cfg4<G, FM, BM, BN, WAVES_M, WAVES_N>;
   constexpr int NS = C::NS;
   constexpr int DW = SHORT ? C::D - 1 : C::D;  // loads this wave issues per stage
+  static_assert(!C::A8 || !COMP, "the E4M3 fallback has no compensation path");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,10 +145,17 @@ __device__ __forceinline__ void gemm_mx4_wave(
     if (k == C::kXRows || k == C::kWRows) {
       const int blk = k == C::kXRows ? g : g - C::XB;
       const int p = blk * 64 + lane;
-      const int r = p >> 2;
-      const int cc = swz<64>(r, p & 3);
-      voff[i] = (uint32_t)min(r0 + r, rmax) * 64u + (uint32_t)(cc * 16);
-      ccol[i] = 8 * cc;
+      if (C::A8 && k == C::kXRows) {  // E4M3 rows: 128 bytes, 8 rows per load
+        const int r = p >> 3;
+        const int cc = swz<128>(r, p & 7);
+        voff[i] = (uint32_t)min(r0 + r, rmax) * 128u + (uint32_t)(cc * 16);
+        ccol[i] = 0;
+      } else {
+        const int r = p >> 2;
+        const int cc = swz<64>(r, p & 3);
+        voff[i] = (uint32_t)min(r0 + r, rmax) * 64u + (uint32_t)(cc * 16);
+        ccol[i] = 8 * cc;
+      }
       dst[i] = (k == C::kXRows ? 0 : C::OFF_B) + blk * 1024;
     } else if (k == C::kXQ || k == C::kWQ) {
       // second region: 32-byte rows, two 16-byte chunks each (the layout permutes the 8-byte
@@ -176,15 +189,15 @@ __device__ __forceinline__ void gemm_mx4_wave(
     // integers, so that every choice stays a scalar select rather than a branch
     const int kp = live ? (comp ? s : s - ncs) : 0;
     const int sp = live && !comp ? (G == 64 ? (s - ncs) >> 1 : s - ncs) : 0;
-    // compensation panels have 64-byte rows, code panels C::CP-byte rows (E3M2 pairs: the first
+    // compensation panels have 64-byte rows, code panels C::CPX / C::CPW-byte rows (E3M2 pairs: the first
     // 64 bytes of every row, then the 32-byte second region of all R rows)
-    const uintptr_t bx = (uintptr_t)(comp ? Bc + (long)kp * (S * 64) : QX + (long)kp * (S * C::CP));
-    const uintptr_t bw = (uintptr_t)(comp ? WL + (long)kp * (N * 64) : QW + (long)kp * (N * C::CP));
-    const uintptr_t bxq = (uintptr_t)(QX + (long)kp * (S * C::CP) + S * 64);
-    const uintptr_t bwq = (uintptr_t)(QW + (long)kp * (N * C::CP) + N * 64);
+    const uintptr_t bx = (uintptr_t)(comp ? Bc + (long)kp * (S * 64) : QX + (long)kp * (S * C::CPX));
+    const uintptr_t bw = (uintptr_t)(comp ? WL + (long)kp * (N * 64) : QW + (long)kp * (N * C::CPW));
+    const uintptr_t bxq = (uintptr_t)(QX + (long)kp * (S * C::CPX) + S * 64);
+    const uintptr_t bwq = (uintptr_t)(QW + (long)kp * (N * C::CPW) + N * 64);
     const uintptr_t bxs = (uintptr_t)(SX + (long)sp * (S * 4));
     const uintptr_t bws = (uintptr_t)(SW + (long)sp * (N * 4));
-    const int nx = live ? S * 64 : 0, nw = live ? N * 64 : 0;
+    const int nx = live ? S * (comp ? 64 : C::XR) : 0, nw = live ? N * 64 : 0;
     const int nxq = live && !comp ? S * 32 : 0, nwq = live && !comp ? N * 32 : 0;  // nothing for compensation
     const int nxs = live ? S * 4 : 0, nws = live ? N * 4 : 0;
     // compensation columns past KC (the padding of the last panel) are loaded from outside the
@@ -252,6 +265,7 @@ __device__ __forceinline__ void gemm_mx4_wave(
   const int qoff1 = lrow * 32 + 8 * ((2 + h) ^ qperm);
   struct Frag {  // one K half of a stage: TM activation and TN weight fragments
     v4i x[C::TM], w[C::TN];
+    v4i x8[C::TM];  // E4M3 activations: the fragments' second 16 bytes
     v8i x6[C::TM], w6[C::TN];  // E3M2 pairs: the whole 24-byte fragments (dwords 6, 7 unused)
   };
   struct Scales {  // a stage's scale dwords, shifted so that byte opsel of the MFMA is the lane's
@@ -266,8 +280,19 @@ __device__ __forceinline__ void gemm_mx4_wave(
     const lds_u8* As = smem + q * C::STAGE;
     const lds_u8* Bs = As + C::OFF_B;
     const int lo = m ? loff1 : loff0;
+    if constexpr (C::A8) {
+      // E4M3: K [64m + 16h, +16) and [64m + 32 + 16h, +16) of the row's 128 bytes, chunks 4m + h and
+      // 4m + 2 + h under the 128-byte-row swizzle
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) f.x[i] = lds4(As + (wm * C::WTM + 32 * i) * 64 + lo);
+      for (int i = 0; i < C::TM; ++i) {
+        const int row = wm * C::WTM + 32 * i + lrow;
+        f.x[i] = lds4(As + row * 128 + (swz<128>(row, 4 * m + h) << 4));
+        f.x8[i] = lds4(As + row * 128 + (swz<128>(row, 4 * m + 2 + h) << 4));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) f.x[i] = lds4(As + (wm * C::WTM + 32 * i) * 64 + lo);
+    }
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) f.w[j] = lds4(Bs + (wn * C::WTN + 32 * j) * 64 + lo);
     if constexpr (C::P6 && !decltype(cs_t)::value) {
@@ -311,6 +336,15 @@ __device__ __forceinline__ void gemm_mx4_wave(
         if (COMP && comp)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, f.w[j]),
                                                               __builtin_bit_cast(v8bf, f.x[i]), acc[i][j], 0, 0, 0);
+        else if (C::A8 && m == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), join(f.x[i], f.x8[i]), acc[i][j],
+                                                                      kFp4, kFp8, 0, sc.w[j], 0, sc.x[i]);
+        else if (C::A8 && G == 32)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), join(f.x[i], f.x8[i]), acc[i][j],
+                                                                      kFp4, kFp8, 2, sc.w[j], 2, sc.x[i]);
+        else if (C::A8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f.w[j]), join(f.x[i], f.x8[i]), acc[i][j],
+                                                                      kFp4, kFp8, 1, sc.w[j], 1, sc.x[i]);
         else if (C::P6 && m == 0)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w6[j], f.x6[i], acc[i][j], kFp6, kFp6, 0,
                                                                       sc.w[j], 0, sc.x[i]);
@@ -332,7 +366,8 @@ __device__ __forceinline__ void gemm_mx4_wave(
       }
   };
   constexpr int NM_H = C::TM * C::TN;   // MFMAs per half-stage
-  constexpr int NF = C::TM + C::TN;     // fragment (or scale) reads per half-stage
+  constexpr int NF = C::TM + C::TN;     // scale reads per stage, fragment reads per half-stage
+  constexpr int NFX = (C::A8 ? 2 : 1) * C::TM + C::TN;  // main-stage fragment reads per half-stage
   // One stage st (not the last): f0 holds its first half's fragments, sc its scales.
   //   top    issue the DMA of stage st + NS - 1, read the second half's fragments of stage st;
   //   half 0 MFMAs on f0;
@@ -352,14 +387,14 @@ __device__ __forceinline__ void gemm_mx4_wave(
     iss(st + NS - 1, smem + qn * C::STAGE);
     read_half(q, 1, f1, cs_t);
     mma(0, f0, sc, CS);
-    Interleave<0, NM_H, DW, (C::P6 && !CS ? 2 : 1) * NF>::run();
+    Interleave<0, NM_H, DW, CS ? NF : (C::P6 ? 2 * NF : NFX)>::run();
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<(NS - 2) * DW>();
     lds_barrier();
     if constexpr (!NCS) read_scales(q1, sr);
     read_half(q1, 0, f0, ncs_t);
     mma(1, f1, sc, CS);
-    Interleave<0, NM_H, 0, NCS ? NF : (C::P6 ? 3 : 2) * NF>::run();
+    Interleave<0, NM_H, 0, NCS ? NF : (C::P6 ? 3 * NF : NF + NFX)>::run();
     if constexpr (!NCS) shift_scales(st + 1, sr, sc);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -405,15 +440,16 @@ __device__ __forceinline__ void gemm_mx4_wave(
       int n;
       uint32_t sa, sb;
       if (k == C::kXRows || k == C::kWRows) {
-        const int R = k == C::kXRows ? S : N;
-        b = (uintptr_t)((k == C::kXRows ? QX : QW) + (long)k0 * (R * C::CP));
-        n = R * 64;
-        sa = sb = (uint32_t)(R * C::CP);
+        const bool xr = k == C::kXRows;
+        const int R = xr ? S : N, cp = xr ? C::CPX : C::CPW;
+        b = (uintptr_t)((xr ? QX : QW) + (long)k0 * (R * cp));
+        n = R * (xr ? C::XR : 64);
+        sa = sb = (uint32_t)(R * cp);
       } else if (C::P6 && (k == C::kXQ || k == C::kWQ)) {
         const int R = k == C::kXQ ? S : N;
-        b = (uintptr_t)((k == C::kXQ ? QX : QW) + (long)k0 * (R * C::CP) + R * 64);
+        b = (uintptr_t)((k == C::kXQ ? QX : QW) + (long)k0 * (R * C::CPX) + R * 64);
         n = R * 32;
-        sa = sb = (uint32_t)(R * C::CP);
+        sa = sb = (uint32_t)(R * C::CPX);
       } else if (k == C::kXScale || k == C::kWScale) {
         const int R = k == C::kXScale ? S : N;
         b = (uintptr_t)((k == C::kXScale ? SX : SW) + (long)(G == 64 ? k0 >> 1 : k0) * (R * 4));
@@ -451,10 +487,10 @@ __device__ __forceinline__ void gemm_mx4_wave(
   // Descriptor sizes and offsets are 32-bit: operands of 2 GiB or more take the general stage path.
   if constexpr (C::P6) {
     const long npan = H / 128;
-    const bool fits = npan * S * C::CP < 0x80000000L && npan * N * C::CP < 0x80000000L;
+    const bool fits = npan * S * C::CPX < 0x80000000L && npan * N * C::CPW < 0x80000000L;
     if (fits && st + NS - 1 < nst) {
       const uint32_t k0 = (uint32_t)(st + NS - 1 - ncs);  // the code panel of the first stage loaded here
-      const uint32_t dX = (uint32_t)(S * C::CP), dW = (uint32_t)(N * C::CP);
+      const uint32_t dX = (uint32_t)(S * C::CPX), dW = (uint32_t)(N * C::CPW);
       const auto rX = panel_rsrc(QX, npan * dX), rW = panel_rsrc(QW, npan * dW);
       const auto rXQ = panel_rsrc(QX + S * 64, npan * dX - S * 64), rWQ = panel_rsrc(QW + N * 64, npan * dW - N * 64);
       uint32_t oX = k0 * dX, oW = k0 * dW;
@@ -621,6 +657,12 @@ hipError_t pick4(const GemmArgs& a, hipStream_t st) {
 }
 
 template <int G, int FM>
+hipError_t pick4_nocomp(const GemmArgs& a, hipStream_t st) {
+  if (a.yt == OSC_Y_F32) return pick4<G, FM, false, OSC_Y_F32>(a, st);
+  return pick4<G, FM, false, OSC_Y_BF16>(a, st);
+}
+
+template <int G, int FM>
 hipError_t pick4_comp(const GemmArgs& a, hipStream_t st) {
   const bool comp = a.B != nullptr;
   if (a.yt == OSC_Y_F32) return comp ? pick4<G, FM, true, OSC_Y_F32>(a, st) : pick4<G, FM, false, OSC_Y_F32>(a, st);
@@ -632,6 +674,7 @@ hipError_t pick4_comp(const GemmArgs& a, hipStream_t st) {
 hipError_t launch_gemm_mx4(const GemmArgs& a, hipStream_t st) {
   if (a.S == 0 || a.N == 0) return hipSuccess;
   if (a.afmt == OSC_FP6P) return pick4_comp<32, kFp6>(a, st);  // E3M2 pairs: 32-wide scale blocks
+  if (a.afmt == OSC_MXFP8) return a.G == 32 ? pick4_nocomp<32, kFp8>(a, st) : pick4_nocomp<64, kFp8>(a, st);
   return a.G == 32 ? pick4_comp<32, kFp4>(a, st) : pick4_comp<64, kFp4>(a, st);
 }
 

@@ -56,8 +56,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // xblk argument; see xcd_tile in osc_device.h).
 int xcd_blocks(int ntm, int ntn, int BM, int BN);
 
-// MXFP4 activations and weights at G = 32 / 64, and the E3M2 pairs, on 32x32 scaled MFMA blocks
-// (the prefill path of launch_gemm for those formats).
+// MXFP4 activations and weights at G = 32 / 64, E4M3 activations with MXFP4 weights (the W2
+// fallback) and the E3M2 pairs, on 32x32 scaled MFMA blocks (the prefill path of launch_gemm for
+// those formats).
 hipError_t launch_gemm_mx4(const GemmArgs& a, hipStream_t st);
 
 // S <= 32 rows: the skinny-S kernel (one 32-column block per workgroup, K split over its waves).
