@@ -397,9 +397,22 @@ __global__ __launch_bounds__(256) void k_quant_blk(const u4* __restrict__ X, int
     // codes: the block's 16 (E2M1) or 32 (E4M3) bytes of the row's 64 / 128 in the panel; scales
     // at G = 16 in panels of 8 groups (this block's two adjacent), else of 4
     if constexpr (FMT == OSC_MXFP8) {
-      u4* dst = reinterpret_cast<u4*>(Q + ((long)p * rows + r) * 128 + b * 32);
-      __builtin_nontemporal_store(u4{codes[0], codes[1], codes[2], codes[3]}, dst);
-      __builtin_nontemporal_store(u4{codes[4], codes[5], codes[6], codes[7]}, dst + 1);
+      // the row's 128 bytes are the four lanes' 32 in lane order: each store writes one contiguous
+      // half row, lane b its bytes [16b, 16b + 16) of the half (from lane 2*half + b/2 of the row's
+      // quad, that lane's first or second 16 bytes by b's parity)
+      u4 lo, hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a0 = __builtin_amdgcn_mov_dpp((int)codes[i], 0x50, 0xF, 0xF, false);      // quad lanes 0,0,1,1
+        const int a1 = __builtin_amdgcn_mov_dpp((int)codes[4 + i], 0x50, 0xF, 0xF, false);
+        const int c0 = __builtin_amdgcn_mov_dpp((int)codes[i], 0xFA, 0xF, 0xF, false);      // quad lanes 2,2,3,3
+        const int c1 = __builtin_amdgcn_mov_dpp((int)codes[4 + i], 0xFA, 0xF, 0xF, false);
+        lo[i] = (uint32_t)((b & 1) ? a1 : a0);
+        hi[i] = (uint32_t)((b & 1) ? c1 : c0);
+      }
+      u4* dst = reinterpret_cast<u4*>(Q + ((long)p * rows + r) * 128 + b * 16);
+      __builtin_nontemporal_store(lo, dst);
+      __builtin_nontemporal_store(hi, dst + 4);
     } else {
       __builtin_nontemporal_store(u4{codes[0], codes[1], codes[2], codes[3]},
                                   reinterpret_cast<u4*>(Q + ((long)p * rows + r) * 64 + b * 16));
